@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against one of: a worked example printed on the
+pages (fixtures under tests/golden/, each carrying its citation), a closed
+form, an invariant between separately computed results, an independent
+library routine (numpy accumulate, numpy/torch float conversions, boolean
+masking), or brute force on tiny inputs.  A mistake in the oracle's fold (a
+dropped term, an off-by-one shift, a wrong identity, a swapped operand in
+min/max, a wrong rounding, a missing wrap) fails at least one of them.
+"""
+import functools
+import itertools
+import math
+import operator
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+INT_DT = {"i32": np.int32, "u32": np.uint32, "i64": np.int64, "u64": np.uint64}
+ALL_DT = ("f32", "f16", "bf16", "f64", "i32", "u32", "i64", "u64")
+
+
+def bits_to_f32(h, dtype):
+    """16-bit patterns -> float32 through torch/numpy (independent of the oracle)."""
+    h = np.asarray(h, dtype=np.uint16)
+    if dtype == "bf16":
+        return torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    return h.view(np.float16).astype(np.float32)
+
+
+def f32_to_bits(x, dtype):
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return workloads.to_bf16_bits(x)
+    return workloads.to_f16_bits(x)
+
+
+def as_float(vals, dtype):
+    """Oracle output -> float64 values, decoding 16-bit formats independently."""
+    if dtype in ("bf16", "f16"):
+        return bits_to_f32(vals, dtype).astype(np.float64)
+    return np.asarray(vals, dtype=np.float64)
+
+
+def random_input(dtype, n, seed):
+    rng = np.random.default_rng(seed)
+    if dtype in ("f32", "f64"):
+        return rng.uniform(-4, 4, size=n).astype(oracle.STORAGE[dtype])
+    if dtype in ("bf16", "f16"):
+        return f32_to_bits(rng.standard_normal(n).astype(np.float32), dtype)
+    info = np.iinfo(INT_DT[dtype])
+    return rng.integers(info.min, info.max, size=n, dtype=INT_DT[dtype], endpoint=True)
+
+
+# ---- worked examples printed on the pages ----------------------------------------
+
+def test_page_exclusive_scan_example(golden):
+    g = golden("exclusive_scan_example.json")
+    x = np.array(g["input"], dtype=np.int32)
+    out = oracle.scan(x, "i32", "add", exclusive=True)
+    assert out.tolist() == g["exclusive"]
+
+
+def test_page_reduce_example(golden):
+    g = golden("reduce_example.json")
+    x = np.array(g["input"], dtype=np.int32)
+    for op in ("add", "min", "max"):
+        inc = oracle.scan(x, "i32", op, exclusive=False)
+        assert int(inc[-1]) == g[op], op           # the inclusive scan ends in the reduction
+
+
+def test_page_select_example(golden):
+    g = golden("select_example.json")
+    out, k = oracle.select(np.array(g["input"], np.int32), np.array(g["flags"], np.uint8))
+    assert k == g["count"]
+    assert out[:k].tolist() == g["selected"]
+
+
+def test_page_order_example(golden):
+    g = golden("order_example.json")
+    for case in g["cases"]:
+        inc = oracle.scan(np.array(case["input"], np.int32), "i32", "add")
+        assert inc.tolist() == case["inclusive"]
+
+
+def test_identities(golden):
+    g = golden("identities.json")
+    for op in ("add", "min", "max"):
+        for dt in ALL_DT:
+            x = random_input(dt, 3, 11)
+            excl = oracle.scan(x, dt, op, exclusive=True)
+            want = g[op][dt]
+            if dt in oracle.FLOATS:
+                got = as_float(excl[:1], dt)[0]
+                want = float(want)
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), (op, dt)
+            else:
+                assert int(excl[0]) == int(want), (op, dt)
+            # the identities agree with numpy's own limits, an independent source
+            if dt in INT_DT and op != "add":
+                info = np.iinfo(INT_DT[dt])
+                assert int(want) == (info.max if op == "min" else info.min)
+
+
+def test_tie_break_signed_zero(golden):
+    g = golden("tie_break.json")
+    for case in g["cases"]:
+        x = np.array([float(v) for v in case["input"]], dtype=np.float32)
+        inc = oracle.scan(x, "f32", case["op"])
+        want = np.array([float(v) for v in case["inclusive"]], dtype=np.float32)
+        assert inc.view(np.uint32).tolist() == want.view(np.uint32).tolist(), case
+
+
+# ---- closed forms -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ALL_DT)
+def test_all_ones(dt):
+    n = 5000
+    if dt in oracle.FLOATS:
+        x = np.ones(n, np.float32)
+        x = f32_to_bits(x, dt) if dt in ("bf16", "f16") else x.astype(oracle.STORAGE[dt])
+    else:
+        x = np.ones(n, INT_DT[dt])
+    inc = oracle.scan(x, dt, "add")
+    exc = oracle.scan(x, dt, "add", exclusive=True)
+    i = np.arange(n)
+    if dt in ("bf16", "f16"):
+        # exact sums i+1 / i, rounded once to the 16-bit format by torch/numpy
+        assert inc.tolist() == f32_to_bits((i + 1).astype(np.float32), dt).tolist()
+        assert exc.tolist() == f32_to_bits(i.astype(np.float32), dt).tolist()
+    else:
+        assert np.array_equal(inc.astype(np.float64), i + 1)
+        assert np.array_equal(exc.astype(np.float64), i)
+
+
+def test_bf16_ones_rounding_ties():
+    # 257 and 259 are halfway between bf16 neighbours: ties go to even
+    x = f32_to_bits(np.ones(300, np.float32), "bf16")
+    inc = bits_to_f32(oracle.scan(x, "bf16", "add"), "bf16")
+    assert inc[256] == 256.0 and inc[258] == 260.0 and inc[255] == 256.0 and inc[259] == 260.0
+
+
+def test_arange_i32_wraps():
+    n = 100_000                                    # n(n-1)/2 ~ 5e9 > 2^32: wraps
+    x = np.arange(n, dtype=np.int32)
+    inc = oracle.scan(x, "i32", "add")
+    exc = oracle.scan(x, "i32", "add", exclusive=True)
+    for i in (0, 1, 2, 65535, 65536, 92681, 92682, n - 1):
+        want_inc = (i * (i + 1) // 2) % (1 << 32)
+        want_exc = (i * (i - 1) // 2) % (1 << 32) if i > 0 else 0
+        assert int(inc[i]) & 0xffffffff == want_inc
+        assert int(exc[i]) & 0xffffffff == want_exc
+    assert (inc.astype(np.int64) < 0).any()        # some prefix did wrap into the sign bit
+
+
+def test_arange_f32_exact():
+    n = 4096                                       # 4095*4096/2 < 2^24: every prefix is exact in f32
+    x = np.arange(n, dtype=np.float32)
+    inc = oracle.scan(x, "f32", "add")
+    i = np.arange(n, dtype=np.float64)
+    assert np.array_equal(inc.astype(np.float64), i * (i + 1) / 2)
+
+
+def test_arange_minmax():
+    n = 1000
+    up = np.arange(n, dtype=np.int64)
+    assert np.array_equal(oracle.scan(up, "i64", "max"), up)
+    assert np.array_equal(oracle.scan(up, "i64", "min"), np.zeros(n, np.int64))
+    down = up[::-1].copy()
+    assert np.array_equal(oracle.scan(down, "i64", "min"), down)
+    assert np.array_equal(oracle.scan(down, "i64", "max"), np.full(n, n - 1, np.int64))
+
+
+# ---- invariants between separately computed results -----------------------------------
+
+@pytest.mark.parametrize("dt", ALL_DT)
+@pytest.mark.parametrize("op", ["add", "min", "max"])
+def test_shift_invariant(dt, op):
+    x = random_input(dt, 777, 3)
+    inc = oracle.scan(x, dt, op)
+    exc = oracle.scan(x, dt, op, exclusive=True)
+    if dt in oracle.FLOATS and op == "add" and dt != "f64":
+        # both are roundings of the same double accumulators: compare those
+        _, ri, _ = oracle.scan(x, dt, op, want_ref=True)
+        _, re, _ = oracle.scan(x, dt, op, exclusive=True, want_ref=True)
+        assert re[0] == 0.0 and np.array_equal(re[1:], ri[:-1])
+    assert np.array_equal(exc[1:].view(np.uint8), inc[:-1].view(np.uint8)) or \
+        exc[1:].tobytes() == inc[:-1].tobytes()
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "i64", "u64"])
+def test_inclusive_is_exclusive_combined_with_input(dt):
+    x = random_input(dt, 1000, 5)
+    for op in ("add", "min", "max"):
+        inc = oracle.scan(x, dt, op)
+        exc = oracle.scan(x, dt, op, exclusive=True)
+        if op == "add":
+            u = np.uint32 if dt in ("i32", "u32") else np.uint64
+            want = (exc.view(u) + x.view(u)).view(INT_DT[dt])   # numpy wraps
+        elif op == "min":
+            want = np.minimum(exc, x)
+        else:
+            want = np.maximum(exc, x)
+        assert np.array_equal(inc, want), op
+
+
+def test_rows_are_independent():
+    x = random_input("f32", 7 * 301, 9).reshape(7, 301)
+    for op in ("add", "min", "max"):
+        for ex in (False, True):
+            whole = oracle.scan(x, "f32", op, exclusive=ex)
+            for r in range(7):
+                assert np.array_equal(whole[r], oracle.scan(x[r].copy(), "f32", op, exclusive=ex))
+
+
+# ---- independent library routines ------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "bf16", "f16"])
+def test_fp_add_matches_numpy_accumulate(dt):
+    x = random_input(dt, 20000, 21)
+    xf = as_float(x, dt)                           # decoded by torch/numpy
+    acc = np.add.accumulate(xf)                    # sequential double fold
+    out, ref, absref = oracle.scan(x, dt, "add", want_ref=True)
+    assert np.array_equal(ref, acc)
+    assert np.array_equal(absref, np.add.accumulate(np.abs(xf)))
+    if dt == "f64":
+        assert np.array_equal(out, acc)
+    elif dt == "f32":
+        assert np.array_equal(out, acc.astype(np.float32))
+    else:
+        assert np.array_equal(out, f32_to_bits(acc.astype(np.float32), dt))
+    _, eref, _ = oracle.scan(x, dt, "add", exclusive=True, want_ref=True)
+    assert eref[0] == 0.0 and np.array_equal(eref[1:], acc[:-1])
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "i64", "u64"])
+def test_int_add_matches_numpy_cumsum(dt):
+    x = random_input(dt, 20000, 23)
+    u = np.uint32 if dt in ("i32", "u32") else np.uint64
+    want = np.cumsum(x.view(u), dtype=u).view(INT_DT[dt])       # wraps mod 2^w
+    assert np.array_equal(oracle.scan(x, dt, "add"), want)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "bf16", "f16", "i32", "u32", "i64", "u64"])
+def test_minmax_match_numpy_accumulate(dt):
+    x = random_input(dt, 20000, 25)
+    xv = as_float(x, dt) if dt in oracle.FLOATS else x
+    for op, uf in (("min", np.minimum), ("max", np.maximum)):
+        got = oracle.scan(x, dt, op)
+        want = uf.accumulate(xv)
+        gv = as_float(got, dt) if dt in oracle.FLOATS else got
+        assert np.array_equal(gv, want), op
+
+
+def test_bf16_rounding_matches_torch():
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.005859375, 1.01171875, 3.4e38,
+                         -3.4e38, 3.3961776e38, 1e-40, -1e-40, 1.4e-45, 65504.0, np.inf, -np.inf,
+                         2.0 ** -126, 2.0 ** -133, 0.1, 1.0 / 3.0], dtype=np.float32)
+    rng = np.random.default_rng(31)
+    rand = (rng.standard_normal(20000) * np.exp(rng.uniform(-80, 80, 20000))).astype(np.float32)
+    bits = rng.integers(0, 1 << 32, size=5000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    bits = bits[np.isfinite(bits)]
+    v = np.concatenate([specials, rand, bits])
+    assert np.array_equal(oracle.f32_to_bf16(v), workloads.to_bf16_bits(v))
+    # NaN: quiet, sign kept
+    q = oracle.f32_to_bf16(np.array([np.nan], np.float32))[0]
+    assert (q & 0x7f80) == 0x7f80 and (q & 0x0040)
+    # widening is exact
+    h = np.arange(0, 1 << 16, 7, dtype=np.uint16)
+    h = h[(h & 0x7f80) != 0x7f80]
+    assert np.array_equal(oracle.bf16_to_f32(h), bits_to_f32(h, "bf16"))
+
+
+def test_f16_rounding_matches_numpy():
+    specials = np.array([0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e6, -1e6,
+                         2.0 ** -14, 2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -26,
+                         3.0 * 2.0 ** -25, 6.1e-5, 1.00048828125, 1.00146484375,
+                         np.inf, -np.inf, 0.1, -2.0 / 3.0], dtype=np.float32)
+    rng = np.random.default_rng(33)
+    rand = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 12, 20000))).astype(np.float32)
+    bits = rng.integers(0, 1 << 32, size=5000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    bits = bits[np.isfinite(bits)]
+    v = np.concatenate([specials, rand, bits])
+    assert np.array_equal(oracle.f32_to_f16(v), workloads.to_f16_bits(v))
+    h = np.arange(0, 1 << 16, 3, dtype=np.uint16)
+    h = h[(h & 0x7c00) != 0x7c00]
+    assert np.array_equal(oracle.f16_to_f32(h), bits_to_f32(h, "f16"))
+
+
+# ---- brute force on tiny inputs -----------------------------------------------------------
+
+def _brute_prefix(vals, dt, op, upto):
+    """Combine vals[0:upto] independently of the oracle."""
+    seq = vals[:upto]
+    if op == "add":
+        if dt in oracle.FLOATS:
+            return functools.reduce(operator.add, [float(v) for v in seq], 0.0)
+        w = 32 if dt in ("i32", "u32") else 64
+        s = sum(int(v) for v in seq) % (1 << w)
+        if dt in ("i32", "i64") and s >= 1 << (w - 1):
+            s -= 1 << w
+        return s
+    if not seq:
+        return None
+    return min(seq) if op == "min" else max(seq)
+
+
+@pytest.mark.parametrize("dt", ALL_DT)
+def test_brute_force_tiny(dt):
+    for n in range(0, 11):
+        x = random_input(dt, n, 100 + n)
+        xv = [float(v) for v in as_float(x, dt)] if dt in oracle.FLOATS else [int(v) for v in x]
+        for op in ("add", "min", "max"):
+            inc = oracle.scan(x, dt, op)
+            exc = oracle.scan(x, dt, op, exclusive=True)
+            for i in range(n):
+                wi = _brute_prefix(xv, dt, op, i + 1)
+                we = _brute_prefix(xv, dt, op, i)
+                gi = as_float(inc[i:i + 1], dt)[0] if dt in oracle.FLOATS else int(inc[i])
+                ge = as_float(exc[i:i + 1], dt)[0] if dt in oracle.FLOATS else int(exc[i])
+                if op == "add" and dt in oracle.FLOATS:
+                    # one rounding of the double fold to the output format
+                    wi = float(as_float(_round_to(dt, wi), dt)[0])
+                    we = float(as_float(_round_to(dt, we), dt)[0])
+                if we is None:                     # empty prefix: the identity
+                    continue
+                assert gi == wi and ge == we, (dt, op, n, i)
+
+
+def _round_to(dt, v):
+    if dt == "f64":
+        return np.array([v], np.float64)
+    f = np.array([v], np.float32)
+    if dt == "f32":
+        return f
+    return f32_to_bits(f, dt)
+
+
+def test_empty_inputs():
+    for dt in ALL_DT:
+        x = np.zeros(0, oracle.STORAGE[dt])
+        assert oracle.scan(x, dt, "add").shape == (0,)
+        assert oracle.scan(np.zeros((0, 5), oracle.STORAGE[dt]), dt, "max").shape == (0, 5)
+    out, k = oracle.select(np.zeros(0, np.float32), np.zeros(0, np.uint8))
+    assert k == 0 and out.shape == (0,)
+
+
+# ---- select ---------------------------------------------------------------------------------
+
+def test_select_every_flag_pattern():
+    n = 10
+    x = np.arange(100, 100 + n, dtype=np.int32)
+    for pattern in itertools.product((0, 1), repeat=n):
+        f = np.array(pattern, np.uint8)
+        out, k = oracle.select(x, f)
+        want = x[f.astype(bool)]
+        assert k == want.size and np.array_equal(out[:k], want)
+        assert not out[k:].any()                   # nothing written past the count
+
+
+def test_select_nonzero_bytes_count_as_selected():
+    x = np.arange(6, dtype=np.int64)
+    f = np.array([0, 2, 255, 0, 1, 128], np.uint8)
+    out, k = oracle.select(x, f)
+    assert k == 4 and out[:k].tolist() == [1, 2, 4, 5]
+
+
+@pytest.mark.parametrize("itemsize", [1, 2, 4, 8, 16])
+def test_select_element_sizes_bit_copy(itemsize):
+    rng = np.random.default_rng(itemsize)
+    n = 3000
+    raw = rng.integers(0, 256, size=n * itemsize, dtype=np.uint8)
+    x = raw.view(np.dtype((np.void, itemsize)))
+    f = (rng.random(n) < 0.3).astype(np.uint8)
+    out, k = oracle.select(x, f)
+    assert out[:k].tobytes() == x[f.astype(bool)].tobytes()
+
+
+def test_select_keeps_nan_payloads():
+    x = np.array([0x7fc00001, 0xffa00002, 0x3f800000], dtype=np.uint32).view(np.float32)
+    out, k = oracle.select(x, np.array([1, 1, 0], np.uint8))
+    assert k == 2 and out[:2].view(np.uint32).tolist() == [0x7fc00001, 0xffa00002]
