@@ -1,0 +1,143 @@
+/*
+ * scan.h - C ABI of the stream_compaction_amd library (libscan_amd.so):
+ * row-wise prefix scan, device-wide exclusive scan and stream compaction on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer (in, out, flags, num_out, scratch) is a DEVICE pointer
+ *    owned by the caller.  The library never allocates, frees or
+ *    synchronizes: all work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream) and the call returns as soon as it
+ *    is enqueued.  Results are visible to later work on the same stream.
+ *    Nothing is read back to the host (the "Algorithms" page, Quadrants user
+ *    guide, section "Key sizing parameters": no host round-trip).
+ *  - Arguments are validated on the host BEFORE anything is enqueued; a
+ *    non-OK status means nothing was launched and no memory was touched.
+ *  - Pointers must be aligned to their element size.  Ranges of different
+ *    arguments must not overlap (SCAN_EALIAS); this refines the rule that an
+ *    exclusive scan's output must be a distinct buffer from its input
+ *    ("Algorithms" page, section qd.algorithms.exclusive_scan_{add,min,max},
+ *    "No in-place scan").
+ *  - Sizes: 0 <= n <= INT32_MAX (the pages index and count with 32-bit
+ *    integers: "Algorithms" page, section "Capacity (log256_max_n)", and the
+ *    i32 count of select).  n == 0 (or rows == 0) is a valid no-op ("Tile
+ *    operations and reductions", section "Why not just infer it from
+ *    reduce?": empty input gives empty output).
+ *  - Scratch ("Algorithms" page, section "Scratch space"): caller-owned, sized
+ *    with the matching *_scratch_bytes() helper (host-only integer
+ *    arithmetic), needs no initialization; the library clears what it needs
+ *    at the start of each call with a small fill kernel on `stream`.  Two
+ *    calls that are in flight at the same time must use different scratch
+ *    buffers.  Scratch must be 16-byte aligned.
+ *  - Identities ("Algorithms" page, section "Common conventions", identity
+ *    value): add 0; min +inf (floats) / INT32_MAX, INT64_MAX / UINT32_MAX,
+ *    UINT64_MAX; max -inf (floats) / INT32_MIN, INT64_MIN / 0.
+ *  - Combine order: the earlier operand is always on the left ("Tile
+ *    operations and reductions", section "Why not just infer it from
+ *    reduce?"); min is (a < b ? a : b) and max is (a > b ? a : b), so a tie
+ *    yields the later element, as in the running-max/min kernels of
+ *    metaltile-std src/mlx/scan.rs.  Integer add wraps modulo 2^w.  min/max
+ *    and integer results are deterministic and exact; floating add may be
+ *    regrouped, so its last bits can differ from a sequential fold ("Algorithms"
+ *    page, "Common conventions", floating-point non-associativity).
+ */
+#ifndef STREAM_COMPACTION_AMD_SCAN_H
+#define STREAM_COMPACTION_AMD_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SCAN_OK = 0,
+    SCAN_EINVAL = 1,    /* bad size, null or misaligned pointer, bad flag value */
+    SCAN_ENOTSUP = 2,   /* dtype/op combination this entry point does not implement */
+    SCAN_EALIAS = 3,    /* two argument ranges overlap */
+    SCAN_ESCRATCH = 4,  /* scratch smaller than *_scratch_bytes() */
+    SCAN_EHIP = 5       /* the HIP runtime refused a launch; see scan_last_hip_error() */
+} scan_status;
+
+/* Element types.  Codes start at 1 so that a zeroed value is rejected. */
+typedef enum {
+    SCAN_F32 = 1, SCAN_F16 = 2, SCAN_BF16 = 3, SCAN_F64 = 4,
+    SCAN_I32 = 5, SCAN_U32 = 6, SCAN_I64 = 7, SCAN_U64 = 8
+} scan_dtype;
+
+typedef enum { SCAN_ADD = 1, SCAN_MIN = 2, SCAN_MAX = 3 } scan_op;
+
+/*
+ * Row-wise scan along the last axis of a contiguous row-major [rows, n]
+ * array (row r starts at element r*n).  Defined in the header comment of
+ * metaltile-std src/mlx/scan.rs: inclusive out[r,i] = op(in[r,0..i]),
+ * exclusive out[r,i] = op(in[r,0..i-1]) with out[r,0] = identity; its
+ * "Multi-op scan variants" comment extends this to min and max.
+ *
+ *   in, out    device pointers, [rows, n] of `dtype`, same layout; must not
+ *              overlap.
+ *   dtype      SCAN_F32, SCAN_F16 or SCAN_BF16 (else SCAN_ENOTSUP).  16-bit
+ *              inputs are widened exactly to float32, accumulated in float32
+ *              (as the kernels of that page cast every load to f32) and each
+ *              output is rounded once to `dtype`, nearest-even ("Tile
+ *              operations and reductions", section "Storage and arithmetic
+ *              precision").
+ *   op         SCAN_ADD, SCAN_MIN or SCAN_MAX.
+ *   exclusive  0 = inclusive, 1 = exclusive (any other value: SCAN_EINVAL).
+ *   rows, n    0 <= rows, n <= INT32_MAX.
+ */
+scan_status scan_rows(const void* in, void* out, int64_t rows, int64_t n,
+                      scan_dtype dtype, scan_op op, int exclusive, void* stream);
+
+/*
+ * Device-wide EXCLUSIVE scan of a flat array ("Algorithms" page, section
+ * qd.algorithms.exclusive_scan_{add,min,max}): out[i] = op(in[0..i-1]),
+ * out[0] = identity(op, dtype).  One pass over the data (single-pass scan
+ * with decoupled look-back between tiles, the alternative that page's
+ * "Related" list names next to the grid-scope fence).
+ *
+ *   in, out    device pointers to n elements of `dtype`; must not overlap.
+ *   dtype      SCAN_I32, SCAN_U32, SCAN_F32, SCAN_I64, SCAN_U64, SCAN_F64
+ *              (the dtype set of that page's "Common conventions").
+ *   op         SCAN_ADD, SCAN_MIN, SCAN_MAX.
+ *   scratch    >= scan_device_scratch_bytes(n, dtype) bytes, 16-byte aligned,
+ *              must not overlap in/out.
+ */
+size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype);
+scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                        void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Stream compaction ("Algorithms" page, section qd.algorithms.select): every
+ * in[i] whose flags[i] is nonzero is copied, in input order, into the dense
+ * prefix out[0..k), and k is written to num_out[0] on the device.  The page
+ * requires flags to be exactly 0/1; here any nonzero byte selects.  out must
+ * hold n elements; out[k..n) is left untouched.  Elements are copied as raw
+ * bytes, so any 4- or 8-byte element type works (NaN payloads survive).
+ *
+ *   in         device pointer, n elements of elem_bytes bytes.
+ *   flags      device pointer, n bytes (uint8).
+ *   out        device pointer, capacity n elements; must not overlap in,
+ *              flags, num_out or scratch.
+ *   num_out    device pointer to one int32.
+ *   elem_bytes 4 or 8 (else SCAN_ENOTSUP).
+ *   scratch    >= select_compact_scratch_bytes(n) bytes, 16-byte aligned.
+ */
+size_t select_compact_scratch_bytes(int64_t n);
+scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                           int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
+                           void* stream);
+
+/* Static string naming a status code (never NULL). */
+const char* scan_status_str(scan_status s);
+
+/* hipError_t value behind the calling thread's last SCAN_EHIP (0 if none). */
+int scan_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAM_COMPACTION_AMD_SCAN_H */

@@ -1,0 +1,194 @@
+"""stream_compaction_amd: prefix scan and stream compaction on an MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libscan_amd.so`` (declared in
+``include/scan.h``).  Every step of every operation runs in the library's HIP
+kernels; this module only turns torch tensors into device pointers, sizes and
+the current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI):
+
+* ``scan_rows(x, op="add", exclusive=False, out=None)`` - scan along the last
+  axis of a contiguous ``[rows, n]`` float32/float16/bfloat16 tensor.
+* ``scan_device(x, op="add", out=None, scratch=None)`` - device-wide exclusive
+  scan of a 1-D int32/uint32/float32/int64/uint64/float64 tensor.
+* ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
+  stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
+* ``scan_device_scratch_bytes(n, dtype)``, ``select_compact_scratch_bytes(n)``.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libscan_amd.so")
+
+# codes of include/scan.h
+_STATUS = {0: "SCAN_OK", 1: "SCAN_EINVAL", 2: "SCAN_ENOTSUP", 3: "SCAN_EALIAS",
+           4: "SCAN_ESCRATCH", 5: "SCAN_EHIP"}
+DTYPE_CODES = {"f32": 1, "f16": 2, "bf16": 3, "f64": 4, "i32": 5, "u32": 6, "i64": 7, "u64": 8}
+OP_CODES = {"add": 1, "min": 2, "max": 3}
+EXPORTS = ("scan_rows", "scan_device", "scan_device_scratch_bytes", "select_compact",
+           "select_compact_scratch_bytes", "scan_status_str", "scan_last_hip_error")
+
+_lib = None
+
+
+class ScanError(RuntimeError):
+    """A HIP runtime failure reported by the library (SCAN_EHIP)."""
+
+
+def lib():
+    """Load libscan_amd.so (built in-tree by ``python -m stream_compaction_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m stream_compaction_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.scan_rows.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp]
+        L.scan_rows.restype = i32
+        L.scan_device_scratch_bytes.argtypes = [i64, i32]
+        L.scan_device_scratch_bytes.restype = sz
+        L.scan_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
+        L.scan_device.restype = i32
+        L.select_compact_scratch_bytes.argtypes = [i64]
+        L.select_compact_scratch_bytes.restype = sz
+        L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
+        L.select_compact.restype = i32
+        L.scan_status_str.argtypes = [i32]
+        L.scan_status_str.restype = ctypes.c_char_p
+        L.scan_last_hip_error.argtypes = []
+        L.scan_last_hip_error.restype = i32
+        _lib = L
+    return _lib
+
+
+def check(status):
+    """Map a scan_status to a Python exception (ValueError / NotImplementedError / ScanError)."""
+    if status == 0:
+        return
+    msg = f"{_STATUS.get(status, status)}: {lib().scan_status_str(status).decode()}"
+    if status == 2:
+        raise NotImplementedError(msg)
+    if status == 5:
+        raise ScanError(f"{msg} (hipError_t {lib().scan_last_hip_error()})")
+    raise ValueError(msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_name(dt):
+    torch = _torch()
+    table = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+             torch.float64: "f64", torch.int32: "i32", torch.int64: "i64"}
+    for name in ("uint32", "uint64"):
+        t = getattr(torch, name, None)
+        if t is not None:
+            table[t] = "u" + name[4:]
+    if dt not in table:
+        raise NotImplementedError(f"dtype {dt} is not supported")
+    return table[dt]
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, what):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_SIZES = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8, "i32": 4, "u32": 4, "i64": 8, "u64": 8}
+
+
+def _name(x, dtype):
+    """Element type name: ``dtype`` if given (e.g. "u32" over an int32 tensor), else x's."""
+    if dtype is None:
+        return dtype_name(x.dtype)
+    if dtype not in _SIZES:
+        raise NotImplementedError(f"dtype {dtype!r} is not supported")
+    if x.element_size() != _SIZES[dtype]:
+        raise ValueError(f"dtype {dtype!r} does not match the tensor's element size")
+    return dtype
+
+
+def scan_rows(x, op="add", exclusive=False, out=None, stream=None, dtype=None):
+    """Row-wise scan along the last axis of ``x`` (viewed as ``[rows, n]``)."""
+    torch = _torch()
+    n = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // n if n else 0
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    check(lib().scan_rows(_dev_ptr(x, "x"), _dev_ptr(out, "out"), rows, n,
+                          DTYPE_CODES[_name(x, dtype)], OP_CODES[op], int(bool(exclusive)),
+                          _stream(stream)))
+    return out
+
+
+def scan_device_scratch_bytes(n, dtype):
+    name = dtype if isinstance(dtype, str) else dtype_name(dtype)
+    return int(lib().scan_device_scratch_bytes(int(n), DTYPE_CODES[name]))
+
+
+def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
+    """Device-wide exclusive scan of the 1-D tensor ``x``."""
+    torch = _torch()
+    if x.dim() != 1:
+        raise ValueError("x must be 1-D")
+    n = x.shape[0]
+    name = _name(x, dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    need = scan_device_scratch_bytes(n, name)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    check(lib().scan_device(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name],
+                            OP_CODES[op], _dev_ptr(scratch, "scratch"), scratch.numel(),
+                            _stream(stream)))
+    return out
+
+
+def select_compact_scratch_bytes(n):
+    return int(lib().select_compact_scratch_bytes(int(n)))
+
+
+def select_compact(x, flags, out=None, num_out=None, scratch=None, stream=None):
+    """Stable compaction of the 1-D tensor ``x`` by nonzero uint8 ``flags``.
+
+    Returns ``(out, num_out)``; ``num_out`` is a 1-element int32 GPU tensor
+    (read it with ``.item()``, which synchronizes).
+    """
+    torch = _torch()
+    if x.dim() != 1 or flags.dim() != 1 or flags.shape[0] != x.shape[0]:
+        raise ValueError("x and flags must be 1-D of the same length")
+    if flags.dtype != torch.uint8:
+        raise ValueError("flags must be uint8")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if out.numel() < n or out.dtype != x.dtype:
+        raise ValueError("out must hold n elements of x's dtype")
+    if num_out is None:
+        num_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    need = select_compact_scratch_bytes(n)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    check(lib().select_compact(_dev_ptr(x, "x"), _dev_ptr(flags, "flags"), _dev_ptr(out, "out"),
+                               _dev_ptr(num_out, "num_out"), n, x.element_size(),
+                               _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
+    return out, num_out

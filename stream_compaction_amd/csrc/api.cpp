@@ -1,0 +1,152 @@
+// C ABI of libscan_amd.so (declared in include/scan.h): host-side validation,
+// then one launcher call.  Nothing here allocates, frees or synchronizes.
+#include "../../include/scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool fmt_of(scan_dtype d, sca::Fmt* f, size_t* bytes) {
+  switch (d) {
+    case SCAN_F32: *f = sca::Fmt::F32; *bytes = 4; return true;
+    case SCAN_F16: *f = sca::Fmt::F16; *bytes = 2; return true;
+    case SCAN_BF16: *f = sca::Fmt::BF16; *bytes = 2; return true;
+    case SCAN_F64: *f = sca::Fmt::F64; *bytes = 8; return true;
+    case SCAN_I32: *f = sca::Fmt::I32; *bytes = 4; return true;
+    case SCAN_U32: *f = sca::Fmt::U32; *bytes = 4; return true;
+    case SCAN_I64: *f = sca::Fmt::I64; *bytes = 8; return true;
+    case SCAN_U64: *f = sca::Fmt::U64; *bytes = 8; return true;
+  }
+  return false;
+}
+
+int op_index(scan_op op) {
+  switch (op) {
+    case SCAN_ADD: return 0;
+    case SCAN_MIN: return 1;
+    case SCAN_MAX: return 2;
+  }
+  return -1;
+}
+
+// Half-open byte ranges [a, a + na) and [b, b + nb) overlap.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round16(size_t b) { return (b + 15) & ~(size_t)15; }
+
+scan_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SCAN_OK;
+  g_last_hip_error = (int)e;
+  return SCAN_EHIP;
+}
+
+constexpr int64_t kMaxN = 2147483647;  // INT32_MAX
+
+}  // namespace
+
+extern "C" {
+
+const char* scan_status_str(scan_status s) {
+  switch (s) {
+    case SCAN_OK: return "ok";
+    case SCAN_EINVAL: return "invalid argument";
+    case SCAN_ENOTSUP: return "unsupported dtype/op";
+    case SCAN_EALIAS: return "argument ranges overlap";
+    case SCAN_ESCRATCH: return "scratch too small";
+    case SCAN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int scan_last_hip_error(void) { return g_last_hip_error; }
+
+scan_status scan_rows(const void* in, void* out, int64_t rows, int64_t n, scan_dtype dtype,
+                      scan_op op, int exclusive, void* stream) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
+  if (fmt != sca::Fmt::F32 && fmt != sca::Fmt::F16 && fmt != sca::Fmt::BF16) return SCAN_ENOTSUP;
+  const int opi = op_index(op);
+  if (opi < 0) return SCAN_ENOTSUP;
+  if (exclusive != 0 && exclusive != 1) return SCAN_EINVAL;
+  if (rows < 0 || n < 0 || rows > kMaxN || n > kMaxN) return SCAN_EINVAL;
+  if (rows == 0 || n == 0) return SCAN_OK;
+  if (in == nullptr || out == nullptr) return SCAN_EINVAL;
+  if (!aligned(in, eb) || !aligned(out, eb)) return SCAN_EINVAL;
+  const size_t bytes = (size_t)rows * (size_t)n * eb;
+  if (overlap(in, bytes, out, bytes)) return SCAN_EALIAS;
+  return hip_status(sca::launch_scan_rows(in, out, rows, n, fmt, opi, exclusive == 1,
+                                          (hipStream_t)stream));
+}
+
+size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb) || n < 0) return 0;
+  return sca::kScratchHeader +
+         round16(sca::scan_device_tiles(n, fmt) * sca::scan_device_desc_words(fmt) * 8);
+}
+
+scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                        void* scratch, size_t scratch_bytes, void* stream) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
+  if (fmt == sca::Fmt::F16 || fmt == sca::Fmt::BF16) return SCAN_ENOTSUP;
+  const int opi = op_index(op);
+  if (opi < 0) return SCAN_ENOTSUP;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
+  if (n == 0) return SCAN_OK;
+  if (in == nullptr || out == nullptr || scratch == nullptr) return SCAN_EINVAL;
+  if (!aligned(in, eb) || !aligned(out, eb) || !aligned(scratch, 16)) return SCAN_EINVAL;
+  const size_t need = scan_device_scratch_bytes(n, dtype);
+  if (scratch_bytes < need) return SCAN_ESCRATCH;
+  const size_t bytes = (size_t)n * eb;
+  if (overlap(in, bytes, out, bytes)) return SCAN_EALIAS;
+  if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes)) return SCAN_EALIAS;
+  return hip_status(sca::launch_scan_device(in, out, n, fmt, opi, scratch, (hipStream_t)stream));
+}
+
+size_t select_compact_scratch_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return sca::kScratchHeader + round16(sca::select_tiles(n, 8) * 8);
+}
+
+scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                           int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
+                           void* stream) {
+  if (elem_bytes != 4 && elem_bytes != 8) return SCAN_ENOTSUP;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
+  if (num_out == nullptr || !aligned(num_out, 4)) return SCAN_EINVAL;
+  if (n > 0) {
+    if (in == nullptr || flags == nullptr || out == nullptr || scratch == nullptr)
+      return SCAN_EINVAL;
+    if (!aligned(in, elem_bytes) || !aligned(out, elem_bytes) || !aligned(scratch, 16))
+      return SCAN_EINVAL;
+    const size_t need = select_compact_scratch_bytes(n);
+    if (scratch_bytes < need) return SCAN_ESCRATCH;
+    const size_t bytes = (size_t)n * elem_bytes;
+    const void* ranges[4] = {in, flags, num_out, scratch};
+    const size_t sizes[4] = {bytes, (size_t)n, 4, need};
+    for (int a = 0; a < 4; ++a)
+      for (int b = a + 1; b < 4; ++b)
+        if (overlap(ranges[a], sizes[a], ranges[b], sizes[b]) && !(a <= 1 && b <= 1))
+          return SCAN_EALIAS;
+    for (int a = 0; a < 4; ++a)
+      if (overlap(out, bytes, ranges[a], sizes[a])) return SCAN_EALIAS;
+  }
+  return hip_status(sca::launch_select(in, flags, out, num_out, n, elem_bytes, scratch,
+                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,398 @@
+// Device building blocks shared by the scan and compaction kernels (gfx950,
+// wave64).  Nothing here is specific to one kernel:
+//   - element formats: storage type, the type the combine runs in, exact
+//     widening and round-to-nearest-even narrowing;
+//   - the combine operators and their identities;
+//   - a 64-lane inclusive scan built from DPP row shifts and row broadcasts;
+//   - 16-byte vector loads/stores over an aligned "window" with element masks;
+//   - tile descriptors for decoupled look-back.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace sca {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Combine operators.  `a` is always the EARLIER operand ("Tile operations and
+// reductions", section "Why not just infer it from reduce?": a noncommutative
+// combine receives the earlier subsequence on its left).  min/max are written
+// as compare+select exactly as the running-max/min kernels of metaltile-std
+// src/mlx/scan.rs do, so ties (e.g. +0 vs -0) yield the later operand; the
+// compiler keeps them as v_cmp + v_cndmask (no v_min/v_max, whose signed-zero
+// rules differ).  Integer add runs in the unsigned type: it wraps mod 2^w.
+// ---------------------------------------------------------------------------
+enum class Op : int { Add = 0, Min = 1, Max = 2 };
+
+template <class T> struct Limits;
+template <> struct Limits<float> {
+  static __device__ __forceinline__ float lowest() { return -__builtin_huge_valf(); }
+  static __device__ __forceinline__ float highest() { return __builtin_huge_valf(); }
+};
+template <> struct Limits<double> {
+  static __device__ __forceinline__ double lowest() { return -__builtin_huge_val(); }
+  static __device__ __forceinline__ double highest() { return __builtin_huge_val(); }
+};
+template <> struct Limits<int32_t> {
+  static __device__ __forceinline__ int32_t lowest() { return INT32_MIN; }
+  static __device__ __forceinline__ int32_t highest() { return INT32_MAX; }
+};
+template <> struct Limits<uint32_t> {
+  static __device__ __forceinline__ uint32_t lowest() { return 0u; }
+  static __device__ __forceinline__ uint32_t highest() { return UINT32_MAX; }
+};
+template <> struct Limits<int64_t> {
+  static __device__ __forceinline__ int64_t lowest() { return INT64_MIN; }
+  static __device__ __forceinline__ int64_t highest() { return INT64_MAX; }
+};
+template <> struct Limits<uint64_t> {
+  static __device__ __forceinline__ uint64_t lowest() { return 0ull; }
+  static __device__ __forceinline__ uint64_t highest() { return UINT64_MAX; }
+};
+
+template <Op O, class W>
+__device__ __forceinline__ W identity() {
+  if constexpr (O == Op::Add) return W(0);
+  else if constexpr (O == Op::Min) return Limits<W>::highest();
+  else return Limits<W>::lowest();
+}
+
+template <class W> struct Unsigned { using type = W; };
+template <> struct Unsigned<int32_t> { using type = uint32_t; };
+template <> struct Unsigned<int64_t> { using type = uint64_t; };
+
+template <Op O, class W>
+__device__ __forceinline__ W combine(W a, W b) {
+  if constexpr (O == Op::Add) {
+    if constexpr (std::is_same_v<W, float> || std::is_same_v<W, double>) {
+      return a + b;
+    } else {
+      using U = typename Unsigned<W>::type;
+      return (W)((U)a + (U)b);
+    }
+  } else if constexpr (O == Op::Min) {
+    return (a < b) ? a : b;
+  } else {
+    return (a > b) ? a : b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Element formats: S is the storage type, W the type the combine runs in.
+// 16-bit floats widen exactly to float32 and narrow with round-to-nearest-even
+// (hardware v_cvt_pk_bf16_f32 / v_cvt_f16_f32 under the default rounding mode),
+// per "Tile operations and reductions", section "Storage and arithmetic
+// precision".
+// ---------------------------------------------------------------------------
+struct FmtF32 { using S = float;    using W = float; };
+struct FmtF16 { using S = uint16_t; using W = float; };
+struct FmtBF16 { using S = uint16_t; using W = float; };
+struct FmtF64 { using S = double;   using W = double; };
+struct FmtI32 { using S = int32_t;  using W = int32_t; };
+struct FmtU32 { using S = uint32_t; using W = uint32_t; };
+struct FmtI64 { using S = int64_t;  using W = int64_t; };
+struct FmtU64 { using S = uint64_t; using W = uint64_t; };
+
+template <class F>
+__device__ __forceinline__ typename F::W widen(typename F::S s) {
+  if constexpr (std::is_same_v<F, FmtBF16>) {
+    return __builtin_bit_cast(float, (uint32_t)s << 16);
+  } else if constexpr (std::is_same_v<F, FmtF16>) {
+    return (float)__builtin_bit_cast(_Float16, s);
+  } else {
+    return s;
+  }
+}
+
+template <class F>
+__device__ __forceinline__ typename F::S narrow(typename F::W w) {
+  if constexpr (std::is_same_v<F, FmtBF16>) {
+    return __builtin_bit_cast(uint16_t, (__bf16)w);
+  } else if constexpr (std::is_same_v<F, FmtF16>) {
+    return __builtin_bit_cast(uint16_t, (_Float16)w);
+  } else {
+    return w;
+  }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two adjacent outputs rounded and packed into one dword (lower address low).
+template <class F>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+  f32x2 v = {a, b};
+  if constexpr (std::is_same_v<F, FmtBF16>) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lane exchange.  DPP moves operate on 32-bit registers; 64-bit values move as
+// two halves.  Lanes whose DPP source is out of range (or whose row is masked
+// off) receive `old`, which callers set to the identity: a shift with a
+// defined boundary fill ("Tile operations and reductions", section "Logical
+// exchange versus physical shuffle").
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK, class W>
+__device__ __forceinline__ W dpp(W src, W old) {
+  if constexpr (sizeof(W) == 4) {
+    return __builtin_bit_cast(W, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, old), __builtin_bit_cast(int, src), CTRL, ROW_MASK, 0xf, false));
+  } else {
+    uint64_t s = __builtin_bit_cast(uint64_t, src), o = __builtin_bit_cast(uint64_t, old);
+    uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)s,
+                                                       CTRL, ROW_MASK, 0xf, false);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32),
+                                                       (int)(uint32_t)(s >> 32), CTRL, ROW_MASK,
+                                                       0xf, false);
+    return __builtin_bit_cast(W, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+template <class W>
+__device__ __forceinline__ W readlane(W v, int lane) {
+  if constexpr (sizeof(W) == 4) {
+    return __builtin_bit_cast(W, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  } else {
+    uint64_t u = __builtin_bit_cast(uint64_t, v);
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(W, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+// DPP control codes (GFX9 encoding).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// Inclusive scan across the 64 lanes (lane i gets v_0 (+) ... (+) v_i).
+// Steps 1-4 scan each 16-lane row (shift right by 1, 2, 4, 8 within the row);
+// row_bcast:15 adds row 0's total into row 1 and row 2's into row 3;
+// row_bcast:31 adds lane 31's prefix into rows 2 and 3.  The value that comes
+// from a lower lane is always the left (earlier) operand.
+template <Op O, class W>
+__device__ __forceinline__ W wave_scan_incl(W v) {
+  const W id = identity<O, W>();
+  v = combine<O>(dpp<kRowShr1, 0xf>(v, id), v);
+  v = combine<O>(dpp<kRowShr2, 0xf>(v, id), v);
+  v = combine<O>(dpp<kRowShr4, 0xf>(v, id), v);
+  v = combine<O>(dpp<kRowShr8, 0xf>(v, id), v);
+  v = combine<O>(dpp<kRowBcast15, 0xa>(v, id), v);
+  v = combine<O>(dpp<kRowBcast31, 0xc>(v, id), v);
+  return v;
+}
+
+// Exclusive scan from an inclusive one: shift by one lane, lane 0 gets the
+// identity.
+template <Op O, class W>
+__device__ __forceinline__ W wave_shift_excl(W incl) {
+  return dpp<kWaveShr1, 0xf>(incl, identity<O, W>());
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+
+// ---------------------------------------------------------------------------
+// Window addressing.  Kernels address an array through a 16-byte-aligned base
+// `abase` that lies `ph` elements before the array's first element; window
+// element index i is array element i - ph.  Vector v of the window covers
+// window elements [v*E, v*E + E) and is a naturally aligned 16-byte block
+// (E = 16 / sizeof(S)).  A vector lying entirely inside the valid range
+// [lo, hi) moves with one 16-byte load/store; a partial vector (ragged row
+// ends, array ends) moves element by element, touching only valid elements.
+// With E == 1 (arrays whose phases differ) every access is one element.
+// ---------------------------------------------------------------------------
+template <class S, int E>
+struct VecIO {
+  static_assert(E == 1 || E * sizeof(S) == 16, "a vector is one element or 16 bytes");
+  // Raw storage bits of one vector.
+  using Raw = std::conditional_t<E == 1, S, uint4>;
+
+  static __device__ __forceinline__ S at(uintptr_t abase, int64_t i) {
+    return *(const S*)(abase + i * sizeof(S));
+  }
+
+  // Storage bits of vector v; elements outside [lo, hi) read as `fill`.
+  static __device__ __forceinline__ Raw load(uintptr_t abase, int64_t v, int64_t lo, int64_t hi,
+                                             S fill) {
+    const int64_t e0 = v * E;
+    if constexpr (E == 1) {
+      return (e0 >= lo && e0 < hi) ? at(abase, e0) : fill;
+    } else {
+      if (e0 >= lo && e0 + E <= hi) return *(const uint4*)(abase + e0 * sizeof(S));
+      S e[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int64_t i = e0 + k;
+        e[k] = (i >= lo && i < hi) ? at(abase, i) : fill;
+      }
+      return __builtin_bit_cast(uint4, e);
+    }
+  }
+
+  template <class F>
+  static __device__ __forceinline__ void unpack(const Raw r, typename F::W (&x)[E]) {
+    if constexpr (E == 1) {
+      x[0] = widen<F>(r);
+    } else {
+      const uint32_t d[4] = {r.x, r.y, r.z, r.w};
+      if constexpr (sizeof(S) == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = widen<F>(__builtin_bit_cast(S, d[k]));
+      } else if constexpr (sizeof(S) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = widen<F>((S)(d[k] & 0xffffu));
+          x[2 * k + 1] = widen<F>((S)(d[k] >> 16));
+        }
+      } else {
+        x[0] = widen<F>(__builtin_bit_cast(S, ((uint64_t)d[1] << 32) | d[0]));
+        x[1] = widen<F>(__builtin_bit_cast(S, ((uint64_t)d[3] << 32) | d[2]));
+      }
+    }
+  }
+
+  template <class F>
+  static __device__ __forceinline__ uint4 pack(const typename F::W (&y)[E]) {
+    uint32_t d[4];
+    if constexpr (sizeof(S) == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = __builtin_bit_cast(uint32_t, narrow<F>(y[k]));
+    } else if constexpr (sizeof(S) == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = narrow2<F>(y[2 * k], y[2 * k + 1]);
+    } else {
+      const uint64_t a = __builtin_bit_cast(uint64_t, narrow<F>(y[0]));
+      const uint64_t b = __builtin_bit_cast(uint64_t, narrow<F>(y[1]));
+      d[0] = (uint32_t)a; d[1] = (uint32_t)(a >> 32);
+      d[2] = (uint32_t)b; d[3] = (uint32_t)(b >> 32);
+    }
+    return uint4{d[0], d[1], d[2], d[3]};
+  }
+
+  // Narrow y and store the elements of vector v that lie in [lo, hi).
+  template <class F>
+  static __device__ __forceinline__ void store(uintptr_t abase, int64_t v, int64_t lo, int64_t hi,
+                                               const typename F::W (&y)[E]) {
+    const int64_t e0 = v * E;
+    if constexpr (E == 1) {
+      if (e0 >= lo && e0 < hi) *(S*)(abase + e0 * sizeof(S)) = narrow<F>(y[0]);
+    } else {
+      if (e0 >= lo && e0 + E <= hi) {
+        *(uint4*)(abase + e0 * sizeof(S)) = pack<F>(y);
+      } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const int64_t i = e0 + k;
+          if (i >= lo && i < hi) *(S*)(abase + i * sizeof(S)) = narrow<F>(y[k]);
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Tile descriptors for decoupled look-back.  Every descriptor word is one
+// 64-bit value written once per call with a single relaxed agent-scope atomic
+// store and read with relaxed agent-scope atomic loads, which on gfx950 are
+// coherent across the XCDs' separate L2 caches.  Because a status and the
+// value it qualifies always travel in the same word, no fence orders them.
+//  - 32-bit values: one word  (status << 32) | value.
+//  - 64-bit values: four words (aggregate lo/hi, inclusive lo/hi), each
+//    (1 << 32) | half; a reader accepts a slot only when both halves are
+//    present, so it never mixes the two slots.
+// Status: 0 = nothing yet, 1 = tile aggregate, 2 = inclusive prefix.
+// A zero-filled descriptor array is the initial state.
+// ---------------------------------------------------------------------------
+enum : uint32_t { kNone = 0, kAgg = 1, kInc = 2 };
+
+__device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class W, int SZ = sizeof(W)> struct Desc;
+
+template <class W> struct Desc<W, 4> {
+  static constexpr int kWords = 1;
+  static __device__ __forceinline__ void publish(uint64_t* d, int64_t tile, uint32_t status, W v) {
+    st_relaxed(d + tile, ((uint64_t)status << 32) | __builtin_bit_cast(uint32_t, v));
+  }
+  // Returns the status; sets v when it is not kNone.
+  static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
+    const uint64_t w = ld_relaxed(d + tile);
+    v = __builtin_bit_cast(W, (uint32_t)w);
+    return (uint32_t)(w >> 32);
+  }
+};
+
+template <class W> struct Desc<W, 8> {
+  static constexpr int kWords = 4;
+  static __device__ __forceinline__ void publish(uint64_t* d, int64_t tile, uint32_t status, W v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    uint64_t* slot = d + tile * 4 + (status == kInc ? 2 : 0);
+    st_relaxed(slot, (1ull << 32) | (uint32_t)u);
+    st_relaxed(slot + 1, (1ull << 32) | (uint32_t)(u >> 32));
+  }
+  static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
+    const uint64_t* s = d + tile * 4;
+    const uint64_t ilo = ld_relaxed(s + 2), ihi = ld_relaxed(s + 3);
+    if ((ilo >> 32) && (ihi >> 32)) {
+      v = __builtin_bit_cast(W, (ihi << 32) | (uint32_t)ilo);
+      return kInc;
+    }
+    const uint64_t alo = ld_relaxed(s), ahi = ld_relaxed(s + 1);
+    if ((alo >> 32) && (ahi >> 32)) {
+      v = __builtin_bit_cast(W, (ahi << 32) | (uint32_t)alo);
+      return kAgg;
+    }
+    return kNone;
+  }
+};
+
+// Look-back by one wave: returns the combine of every tile before `tile`
+// (the tile's exclusive prefix).  Lane l inspects tile base - 63 + l, so lane
+// order is tile order and lane 63 is the nearest predecessor.  Each round
+// waits until the lanes above the nearest inclusive descriptor (or all lanes,
+// if there is none) hold at least an aggregate, reduces lanes
+// [nearest inclusive .. 63] in order with the wave scan, and prepends the
+// result to what later windows already gave.  Tiles before 0 read as
+// inclusive identities, so the walk always ends.
+template <Op O, class W>
+__device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile) {
+  const int lane = lane_id();
+  const W id = identity<O, W>();
+  W prefix = id;
+  for (int64_t base = tile - 1;; base -= kWave) {
+    const int64_t t = base - (kWave - 1) + lane;
+    W v = id;
+    uint32_t st;
+    for (;;) {
+      st = (t < 0) ? (uint32_t)kInc : Desc<W>::read(desc, t, v);
+      if (t < 0) v = id;
+      const uint64_t inc = __ballot(st == kInc);
+      const uint64_t none = __ballot(st == kNone);
+      const uint64_t need = inc ? (~0ull << (63 - __builtin_clzll(inc))) : ~0ull;
+      if ((none & need) == 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const uint64_t inc = __ballot(st == kInc);
+    const int stop = inc ? 63 - __builtin_clzll(inc) : 0;
+    if (lane < stop) v = id;
+    const W window = readlane(wave_scan_incl<O>(v), kWave - 1);
+    prefix = combine<O>(window, prefix);
+    if (inc) return prefix;
+  }
+}
+
+}  // namespace sca

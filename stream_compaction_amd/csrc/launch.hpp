@@ -1,0 +1,41 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernel
+// translation units.  Arguments reaching these launchers are already
+// validated; each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sca {
+
+enum class Fmt : int { F32, F16, BF16, F64, I32, U32, I64, U64 };
+
+// Workgroup size of every kernel (four wave64s).
+constexpr int kBlock = 256;
+
+// Row-wise scan; op: 0 add, 1 min, 2 max.
+hipError_t launch_scan_rows(const void* in, void* out, int64_t rows, int64_t n, Fmt fmt, int op,
+                            bool exclusive, hipStream_t stream);
+
+// Device-wide exclusive scan.
+size_t scan_device_tiles(int64_t n, Fmt fmt);       // descriptors needed
+size_t scan_device_desc_words(Fmt fmt);             // 64-bit words per descriptor
+hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
+                              void* scratch, hipStream_t stream);
+
+// Stream compaction.
+size_t select_tiles(int64_t n, size_t elem_bytes);
+hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                         int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream);
+
+// Scratch layout shared by the look-back kernels: a 256-byte header whose
+// first dword is the dynamic tile counter, then the descriptor words.
+constexpr size_t kScratchHeader = 256;
+
+// Zero `bytes` rounded up to a multiple of 16 at a 16-byte-aligned device
+// address (scratch sizes are rounded the same way) with a small fill kernel
+// (no hipMemsetAsync, so the call can sit in a captured graph).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace sca

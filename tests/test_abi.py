@@ -1,0 +1,133 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+that include/scan.h declares, and rejects bad arguments on the host before
+anything touches a GPU (so these run without one).  The pointers below are
+fake addresses: every call here returns from host validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import stream_compaction_amd as sc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "scan.h")
+
+OK, EINVAL, ENOTSUP, EALIAS, ESCRATCH = 0, 1, 2, 3, 4
+D = sc.DTYPE_CODES
+OP = sc.OP_CODES
+A = 0x10000000            # fake, 256-byte aligned "device" addresses
+B = 0x20000000
+S = 0x30000000
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(sc.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sc.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_enum_codes_match_header():
+    text = open(HDR).read()
+    for name, code in D.items():
+        assert re.search(rf"SCAN_{name.upper()} = {code}\b", text), name
+    for name, code in OP.items():
+        assert re.search(rf"SCAN_{name.upper()} = {code}\b", text), name
+
+
+def test_status_strings():
+    L = sc.lib()
+    for s in range(6):
+        assert L.scan_status_str(s)
+    assert L.scan_status_str(99) == b"unknown status"
+    assert L.scan_last_hip_error() == 0
+
+
+def rows(*args):
+    return sc.lib().scan_rows(*args)
+
+
+def test_scan_rows_validation():
+    f32 = D["f32"]
+    add = OP["add"]
+    assert rows(A, B, 4, 16, D["i32"], add, 0, None) == ENOTSUP     # row scan is float-only
+    assert rows(A, B, 4, 16, 0, add, 0, None) == ENOTSUP            # zeroed dtype code
+    assert rows(A, B, 4, 16, f32, 0, 0, None) == ENOTSUP            # zeroed op code
+    assert rows(A, B, 4, 16, f32, add, 2, None) == EINVAL           # exclusive must be 0/1
+    assert rows(A, B, -1, 16, f32, add, 0, None) == EINVAL
+    assert rows(A, B, 4, -16, f32, add, 0, None) == EINVAL
+    assert rows(A, B, 4, 1 << 31, f32, add, 0, None) == EINVAL      # n > INT32_MAX
+    assert rows(None, B, 4, 16, f32, add, 0, None) == EINVAL
+    assert rows(A + 2, B, 4, 16, f32, add, 0, None) == EINVAL       # not element aligned
+    assert rows(A, B + 1, 4, 16, D["bf16"], add, 0, None) == EINVAL
+    assert rows(A, A + 64, 4, 16, f32, add, 0, None) == EALIAS      # 256 B ranges overlap
+    assert rows(A, A, 1, 1, f32, add, 0, None) == EALIAS            # in place
+    # empty shapes are no-ops that never launch (no GPU needed)
+    assert rows(A, B, 0, 16, f32, add, 0, None) == OK
+    assert rows(A, B, 4, 0, f32, add, 0, None) == OK
+    assert rows(None, None, 0, 0, f32, add, 1, None) == OK
+
+
+def test_scan_device_validation():
+    L = sc.lib()
+    i32 = D["i32"]
+    add = OP["add"]
+    need = L.scan_device_scratch_bytes(1000, i32)
+    assert need >= 256 and need % 16 == 0
+    assert L.scan_device_scratch_bytes(-1, i32) == 0
+    assert L.scan_device(A, B, 1000, D["bf16"], add, S, need, None) == ENOTSUP
+    assert L.scan_device(A, B, 1000, i32, 7, S, need, None) == ENOTSUP
+    assert L.scan_device(A, B, -1, i32, add, S, need, None) == EINVAL
+    assert L.scan_device(A, B, 1 << 31, i32, add, S, need, None) == EINVAL
+    assert L.scan_device(A, B, 1000, i32, add, None, need, None) == EINVAL
+    assert L.scan_device(A, B, 1000, i32, add, S + 8, need, None) == EINVAL   # scratch alignment
+    assert L.scan_device(A, B + 2, 1000, i32, add, S, need, None) == EINVAL
+    assert L.scan_device(A, B, 1000, i32, add, S, need - 1, None) == ESCRATCH
+    assert L.scan_device(A, A + 3996, 1000, i32, add, S, need, None) == EALIAS
+    assert L.scan_device(A, B, 1000, i32, add, A + 256, need, None) == EALIAS  # scratch in `in`
+    assert L.scan_device(A, B, 0, i32, add, None, 0, None) == OK
+    # scratch grows with n and is sized for every dtype and alignment
+    for name in ("i32", "u32", "f32", "i64", "u64", "f64"):
+        small = L.scan_device_scratch_bytes(1 << 20, D[name])
+        big = L.scan_device_scratch_bytes(1 << 28, D[name])
+        assert big > small > 0
+        assert big < (1 << 28) // 64                 # a small fraction of the data
+
+
+def test_select_validation():
+    L = sc.lib()
+    need = L.select_compact_scratch_bytes(1000)
+    N = B + 0x100000
+    assert L.select_compact(A, S + 0x1000, B, N, 1000, 2, S, need, None) == ENOTSUP
+    assert L.select_compact(A, S + 0x1000, B, N, 1000, 16, S, need, None) == ENOTSUP
+    assert L.select_compact(A, S + 0x1000, B, None, 1000, 4, S, need, None) == EINVAL
+    assert L.select_compact(A, S + 0x1000, B, N + 2, 1000, 4, S, need, None) == EINVAL
+    assert L.select_compact(A, S + 0x10000, B, N, -5, 4, S, need, None) == EINVAL
+    assert L.select_compact(None, S + 0x10000, B, N, 1000, 4, S, need, None) == EINVAL
+    assert L.select_compact(A, S + 0x10000, B, N, 1000, 4, S, need - 16, None) == ESCRATCH
+    assert L.select_compact(A, S + 0x10000, A + 100, N, 1000, 4, S, need, None) == EALIAS
+    assert L.select_compact(A, S + 0x10000, B, B + 40, 1000, 4, S, need, None) == EALIAS
+    assert L.select_compact(A, S + 16, B, N, 1000, 4, S, need, None) == EALIAS   # flags in scratch
+
+
+def test_binding_maps_status_to_exceptions():
+    with pytest.raises(ValueError):
+        sc.check(EINVAL)
+    with pytest.raises(NotImplementedError):
+        sc.check(ENOTSUP)
+    with pytest.raises(ValueError):
+        sc.check(EALIAS)
+    with pytest.raises(sc.ScanError):
+        sc.check(5)
+    sc.check(OK)

@@ -1,0 +1,387 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case draws seeded inputs from workloads.py, runs the library on the GPU
+and the oracle on the host, and compares element by element: bit-exact for
+integer and min/max scans and for select (count, prefix and untouched tail),
+within the float-add tolerance of tests/parity.py otherwise.  The full-size
+cases are the five workloads at their stated sizes, in the same launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_compaction_amd as sc
+import workloads
+from parity import check_exact, check_fp_add, decode16
+
+pytestmark = pytest.mark.gpu
+
+STORE_T = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "f64": torch.float64, "i32": torch.int32, "u32": torch.int32, "i64": torch.int64,
+           "u64": torch.int64}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dt):
+    """numpy storage array -> GPU tensor (bf16/f16 bits reinterpret; u32/u64 ride in int32/int64)."""
+    a = np.ascontiguousarray(a)
+    if dt == "bf16":
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    if dt == "f16":
+        return torch.from_numpy(a.view(np.float16).copy()).cuda()
+    if dt in ("u32", "u64"):
+        return torch.from_numpy(a.view(np.int32 if dt == "u32" else np.int64).copy()).cuda()
+    return torch.from_numpy(a.copy()).cuda()
+
+
+def from_dev(t, dt):
+    t = t.cpu()
+    if dt in ("bf16", "f16"):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    a = t.numpy()
+    if dt == "u32":
+        return a.view(np.uint32)
+    if dt == "u64":
+        return a.view(np.uint64)
+    return a
+
+
+def rand_input(dt, shape, seed):
+    rng = np.random.default_rng(seed)
+    if dt in ("f32", "f64"):
+        return rng.uniform(-1, 1, size=shape).astype(oracle.STORAGE[dt])
+    if dt == "bf16":
+        return workloads.normal_bf16(shape, seed)
+    if dt == "f16":
+        return workloads.to_f16_bits(rng.standard_normal(size=shape).astype(np.float32))
+    info = np.iinfo(oracle.STORAGE[dt])
+    if dt in ("i32", "u32"):
+        # small values so add scans stay in range on some cases and wrap on others
+        return rng.integers(info.min, info.max, size=shape, dtype=oracle.STORAGE[dt], endpoint=True)
+    return rng.integers(info.min, info.max, size=shape, dtype=oracle.STORAGE[dt], endpoint=True)
+
+
+def compare_scan(gpu, x, dt, op, exclusive, label):
+    if op == "add" and dt in oracle.FLOATS:
+        ora, ref, absref = oracle.scan(x, dt, op, exclusive=exclusive, want_ref=True)
+        return check_fp_add(gpu, ora, ref, absref, dt, label)
+    ora = oracle.scan(x, dt, op, exclusive=exclusive)
+    check_exact(gpu, ora, label)
+    return None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# row-wise scans
+# ---------------------------------------------------------------------------
+
+ROW_SHAPES = [(1, 1), (1, 2), (3, 3), (3, 5), (1, 63), (3, 64), (5, 65), (3, 255), (3, 256),
+              (3, 257), (2, 511), (3, 513), (2, 1023), (2, 1024), (3, 1025), (2, 2047), (3, 2049),
+              (2, 4351), (2, 4352), (3, 4353), (2, 8703), (2, 8704), (3, 8705), (2, 20000),
+              (7, 333), (33, 100)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["add", "min", "max"])
+@pytest.mark.parametrize("excl", [False, True], ids=["incl", "excl"])
+def test_rows_shapes(dt, op, excl):
+    for i, (rows, n) in enumerate(ROW_SHAPES):
+        label = f"scan_rows {dt} {op} excl={excl} [{rows},{n}]"
+        x = rand_input(dt, (rows, n), 1000 + i)
+        out = sc.scan_rows(to_dev(x, dt), op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        compare_scan(from_dev(out, dt), x, dt, op, excl, label)
+
+
+def test_rows_workload1_full():
+    rows, n = workloads.FULL["rows_f32"]
+    x = workloads.rows_f32(rows, n)
+    xd = to_dev(x, "f32")
+    for excl in (False, True):
+        label = f"scan_rows f32 add excl={excl} [{rows},{n}]"
+        note(label)
+        out = sc.scan_rows(xd, op="add", exclusive=excl)
+        torch.cuda.synchronize()
+        err, ratio = compare_scan(from_dev(out, "f32"), x, "f32", "add", excl, label)
+        note(f"  max abs err {err:.3g}, max err/bound {ratio:.3g}")
+
+
+@pytest.mark.parametrize("shape", [workloads.FULL["rows_bf16"], workloads.FULL["rows_bf16_ragged"]],
+                         ids=["8192x8192", "8192x8191"])
+def test_rows_workload2_full(shape):
+    rows, n = shape
+    x = workloads.rows_bf16(rows, n)
+    label = f"scan_rows bf16 add excl [{rows},{n}]"
+    note(label)
+    out = sc.scan_rows(to_dev(x, "bf16"), op="add", exclusive=True)
+    torch.cuda.synchronize()
+    err, ratio = compare_scan(from_dev(out, "bf16"), x, "bf16", "add", True, label)
+    note(f"  max abs err {err:.3g}, max err/bound {ratio:.3g}")
+
+
+@pytest.mark.parametrize("excl", [False, True], ids=["incl", "excl"])
+def test_rows_bf16_ones_closed_form_full(excl):
+    # float32 sums of ones are exact (< 2^24): each output is the bf16 rounding
+    # of its index (+1), ties to even (257 -> 256, 259 -> 260), bit for bit.
+    rows, n = workloads.FULL["rows_bf16"]
+    x = torch.ones((rows, n), dtype=torch.bfloat16, device="cuda")
+    out = sc.scan_rows(x, op="add", exclusive=excl)
+    i = torch.arange(n, dtype=torch.float32) + (0 if excl else 1)
+    want = i.to(torch.bfloat16).view(torch.int16)
+    got = out.view(torch.int16).cpu()
+    assert torch.equal(got, want.expand(rows, n))
+
+
+def test_rows_misaligned_views():
+    # element offsets move the arrays off 16-byte alignment, with equal and unequal phases
+    for dt in ("f32", "bf16"):
+        for off_in, off_out in ((1, 1), (3, 3), (1, 2), (0, 3), (5, 0)):
+            rows, n = 5, 1234
+            x = rand_input(dt, (rows * n,), 77)
+            big_in = torch.zeros(rows * n + 8, dtype=STORE_T[dt], device="cuda")
+            big_out = torch.zeros(rows * n + 8, dtype=STORE_T[dt], device="cuda")
+            xin = big_in[off_in:off_in + rows * n]
+            xin.copy_(to_dev(x, dt))
+            yout = big_out[off_out:off_out + rows * n]
+            for op in ("add", "max"):
+                for excl in (False, True):
+                    sc.scan_rows(xin.view(rows, n), op=op, exclusive=excl, out=yout.view(rows, n))
+                    torch.cuda.synchronize()
+                    compare_scan(from_dev(yout, dt).reshape(rows, n), x.reshape(rows, n), dt, op,
+                                 excl, f"misaligned {dt} {op} in+{off_in} out+{off_out}")
+            # nothing outside the output view was written
+            assert not big_out[:off_out].any() and not big_out[off_out + rows * n:].any()
+
+
+def test_rows_signed_zero_and_inf():
+    vals = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0], np.float32)
+    rng = np.random.default_rng(5)
+    x = vals[rng.integers(0, len(vals), size=(4, 3000))]
+    for op in ("min", "max"):
+        for excl in (False, True):
+            out = sc.scan_rows(to_dev(x, "f32"), op=op, exclusive=excl)
+            compare_scan(from_dev(out, "f32"), x, "f32", op, excl, f"signed zeros {op}")
+
+
+def test_rows_empty():
+    for shape in ((0, 5), (5, 0), (0, 0)):
+        x = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        out = sc.scan_rows(x)
+        assert out.shape == shape
+
+
+# ---------------------------------------------------------------------------
+# device-wide exclusive scan
+# ---------------------------------------------------------------------------
+
+DEV_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 8191, 8192, 8193,
+             16383, 16384, 16385, 2 * 16384 + 37, 300_001, 1_000_003, 1_500_001]
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "f32", "i64", "u64", "f64"])
+@pytest.mark.parametrize("op", ["add", "min", "max"])
+def test_device_sizes(dt, op):
+    for i, n in enumerate(DEV_SIZES):
+        label = f"scan_device {dt} {op} n={n}"
+        x = rand_input(dt, n, 2000 + i)
+        out = sc.scan_device(to_dev(x, dt), op=op, dtype=dt)
+        torch.cuda.synchronize()
+        compare_scan(from_dev(out, dt), x, dt, op, True, label)
+
+
+@pytest.mark.parametrize("n", [workloads.FULL["dev_i32"], workloads.FULL["dev_i32_odd"]],
+                         ids=["2^28", "2^28-37"])
+def test_device_workload3_full(n):
+    x = workloads.dev_i32()[:n]
+    label = f"scan_device i32 add n={n}"
+    note(label)
+    out = sc.scan_device(to_dev(x, "i32"), op="add")
+    torch.cuda.synchronize()
+    compare_scan(from_dev(out, "i32"), x, "i32", "add", True, label)
+
+
+def test_device_arange_wraps_full():
+    # closed form: exclusive sum of 0..i-1 = i(i-1)/2, reduced mod 2^32
+    n = workloads.FULL["dev_i32"]
+    x = torch.arange(n, dtype=torch.int32, device="cuda")
+    out = sc.scan_device(x, op="add").cpu().numpy().view(np.uint32)
+    i = np.arange(n, dtype=np.uint64)
+    want = ((i * (i - np.uint64(1))) // np.uint64(2)) & np.uint64(0xffffffff)
+    want[0] = 0
+    assert np.array_equal(out.astype(np.uint64), want)
+
+
+def test_device_ones_full():
+    n = workloads.FULL["dev_i32"]
+    out = sc.scan_device(torch.ones(n, dtype=torch.int32, device="cuda"), op="add")
+    assert torch.equal(out.cpu(), torch.arange(n, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("which", ["f32", "i64"])
+@pytest.mark.parametrize("op", ["min", "max"])
+def test_device_workload4_full(which, op):
+    x = workloads.dev_f32() if which == "f32" else workloads.dev_i64()
+    label = f"scan_device {which} {op} n={x.size}"
+    note(label)
+    out = sc.scan_device(to_dev(x, which), op=op)
+    torch.cuda.synchronize()
+    compare_scan(from_dev(out, which), x, which, op, True, label)
+
+
+def test_device_misaligned_views():
+    for dt in ("i32", "i64", "f32"):
+        for off_in, off_out in ((1, 1), (1, 0), (0, 3), (2, 2)):
+            n = 100_003
+            x = rand_input(dt, n, 99)
+            big_in = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+            big_out = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+            xin = big_in[off_in:off_in + n]
+            xin.copy_(to_dev(x, dt))
+            yout = big_out[off_out:off_out + n]
+            for op in ("add", "min"):
+                sc.scan_device(xin, op=op, out=yout)
+                torch.cuda.synchronize()
+                compare_scan(from_dev(yout, dt), x, dt, op, True,
+                             f"misaligned scan_device {dt} {op} in+{off_in} out+{off_out}")
+            assert not big_out[:off_out].any() and not big_out[off_out + n:].any()
+
+
+def test_device_repeated_calls_reuse_scratch():
+    rng = np.random.default_rng(7)
+    nmax = 3_000_000
+    scratch = torch.empty(sc.scan_device_scratch_bytes(nmax, "i32"), dtype=torch.uint8,
+                          device="cuda")
+    scratch.fill_(0xAB)                     # no initialization is required of the caller
+    for it in range(12):
+        n = int(rng.integers(1, nmax))
+        x = workloads.uniform_ints(n, 0, 15, 300 + it)
+        out = sc.scan_device(to_dev(x, "i32"), op="add", scratch=scratch)
+        torch.cuda.synchronize()
+        compare_scan(from_dev(out, "i32"), x, "i32", "add", True, f"repeat {it} n={n}")
+
+
+def test_device_two_streams():
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    n = 2_000_000
+    xa = workloads.uniform_ints(n, 0, 15, 41)
+    xb = workloads.uniform_ints(n, 0, 15, 42)
+    da, db = to_dev(xa, "i32"), to_dev(xb, "i32")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        oa = sc.scan_device(da, op="add")
+    with torch.cuda.stream(s2):
+        ob = sc.scan_device(db, op="add")
+    torch.cuda.synchronize()
+    compare_scan(from_dev(oa, "i32"), xa, "i32", "add", True, "stream 1")
+    compare_scan(from_dev(ob, "i32"), xb, "i32", "add", True, "stream 2")
+
+
+def test_device_signed_zero_and_inf():
+    vals = np.array([0.0, -0.0, np.inf, -np.inf, 2.0, -2.0], np.float32)
+    x = vals[np.random.default_rng(6).integers(0, len(vals), size=200_000)]
+    for op in ("min", "max"):
+        out = sc.scan_device(to_dev(x, "f32"), op=op)
+        compare_scan(from_dev(out, "f32"), x, "f32", op, True, f"scan_device signed zeros {op}")
+
+
+# ---------------------------------------------------------------------------
+# select
+# ---------------------------------------------------------------------------
+
+SEL_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 8191, 8192, 8193,
+             20_000, 1_000_003]
+SENTINEL = {4: 0x5A5A5A5A, 8: 0x5A5A5A5A5A5A5A5A}
+
+
+def run_select(x, flags, eb, label):
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int32 if eb == 4 else np.int64).copy()).cuda()
+    fd = torch.from_numpy(flags.copy()).cuda()
+    out = torch.full((n,), SENTINEL[eb], dtype=xd.dtype, device="cuda")
+    out, num = sc.select_compact(xd, fd, out=out)
+    torch.cuda.synchronize()
+    k = int(num.item())
+    ora, ko = oracle.select(x, flags)
+    assert k == ko, f"{label}: count {k} != {ko}"
+    got = out.cpu().numpy().view(x.dtype)
+    check_exact(got[:k], ora[:k], label)
+    tail = out.cpu().numpy()[k:]
+    assert (tail.view(np.uint32 if eb == 4 else np.uint64) == SENTINEL[eb]).all(), \
+        f"{label}: tail written"
+    return k
+
+
+@pytest.mark.parametrize("eb", [4, 8])
+@pytest.mark.parametrize("p", [0.0, 0.01, 0.5, 0.99, 1.0])
+def test_select_sizes(eb, p):
+    for i, n in enumerate(SEL_SIZES):
+        rng = np.random.default_rng(3000 + i)
+        x = rng.integers(0, 1 << 62, size=n, dtype=np.int64)
+        x = x.astype(np.uint32) if eb == 4 else x.astype(np.uint64)
+        flags = workloads.bernoulli_flags(n, p, 4000 + i)
+        run_select(x, flags, eb, f"select eb={eb} p={p} n={n}")
+
+
+@pytest.mark.parametrize("p", workloads.SELECT_P)
+def test_select_workload5_full(p):
+    payload, flags = workloads.sel_inputs(workloads.FULL["sel"], p)
+    label = f"select f32 n={payload.size} p={p}"
+    note(label)
+    k = run_select(payload, flags, 4, label)
+    note(f"  kept {k}")
+
+
+def test_select_nonbinary_flags_and_nan_payloads():
+    n = 50_000
+    rng = np.random.default_rng(8)
+    flags = rng.integers(0, 256, size=n, dtype=np.uint8)
+    flags[rng.random(n) < 0.5] = 0
+    x = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    x[::7] = 0x7fc00001                      # NaN with a payload
+    run_select(x, flags, 4, "select nonbinary flags")
+
+
+def test_select_misaligned_views():
+    n = 100_003
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 1 << 31, size=n, dtype=np.int64).astype(np.int32)
+    flags = workloads.bernoulli_flags(n, 0.5, 10)
+    ora, ko = oracle.select(x, flags)
+    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1)):
+        big_in = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
+        big_f = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+        big_out = torch.full((n + 8,), 7, dtype=torch.int32, device="cuda")
+        xin = big_in[off_in:off_in + n]
+        xin.copy_(torch.from_numpy(x).cuda())
+        fin = big_f[off_f:off_f + n]
+        fin.copy_(torch.from_numpy(flags).cuda())
+        yout = big_out[off_out:off_out + n]
+        _, num = sc.select_compact(xin, fin, out=yout)
+        k = int(num.item())
+        assert k == ko
+        got = big_out.cpu().numpy()
+        check_exact(got[off_out:off_out + k], ora[:k], f"select offsets {off_in},{off_f},{off_out}")
+        assert (got[:off_out] == 7).all() and (got[off_out + k:] == 7).all()
+
+
+def test_select_empty():
+    x = torch.zeros(0, dtype=torch.float32, device="cuda")
+    f = torch.zeros(0, dtype=torch.uint8, device="cuda")
+    num = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+    sc.select_compact(x, f, num_out=num)
+    assert int(num.item()) == 0
