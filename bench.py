@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the scan library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAMES] [--no-cpu]
+
+A step is one call of the library on one batch of synthetic input resident in
+HBM.  The headline step is the row-wise exclusive add scan of a bf16
+[8192, 8192] array (N(0,1), seed 1; float32 accumulation, bf16 output rounded
+to nearest even).  Consecutive steps rotate over several input/output buffer
+pairs so that no step finds its data in the 256 MB Infinity Cache left there
+by the previous one.  The other workloads (row scans of fp32 [1024, 4096] and
+bf16 [8192, 8191], the device-wide scans and select) are timed the same way
+and reported inside the same JSON line under "workloads".
+
+Prints ONE JSON line.  "value" is elements/s of the headline workload (wall
+clock over the K timed steps); "roofline" rates the headline kernel by its
+algorithmic bytes (read n + write n) over its average launch duration from HIP
+events; "cpu_baseline" times the CPU oracle on the same workload on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
+METRIC = "scan elements/s and achieved HBM GB/s (% of peak), 1 MI355X"
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = {           # sources whose change invalidates stored counter readings
+    "scan_rows": ["device.hpp", "scan_rows.hip"],
+    "scan_device": ["device.hpp", "scan_device.hip"],
+    "select": ["device.hpp", "select.hip"],
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sub-steps", type=int, default=20, help="timed calls per other workload")
+    ap.add_argument("--sets", type=int, default=4, help="buffer sets rotated between steps")
+    ap.add_argument("--only", default="", help="comma-separated workload names to run (profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def sources_sha(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "stream_compaction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU: the library has no multi-GPU "
+                                   "path, so --gpus must be 1", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import stream_compaction_amd as sc
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sc.lib()
+    only = set(filter(None, args.only.split(",")))
+
+    def want(name):
+        return not only or name in only
+
+    def timed(launch, steps, warmup):
+        """Run launch(i) warmup+steps times; returns (wall seconds, per-launch ms list)."""
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev0[i].record(stream)
+            launch(i)
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+
+    def bf16_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    results = {}
+
+    def record(name, elems, algo_bytes, wall, per_ms, steps, note=""):
+        avg_ms = float(np.mean(per_ms))
+        r = {"elements": int(elems), "algorithmic_bytes": int(algo_bytes),
+             "kernel_ms_avg": round(avg_ms, 5), "kernel_ms_min": round(float(np.min(per_ms)), 5),
+             "elements_per_s": elems / (avg_ms * 1e-3),
+             "GBps": algo_bytes / (avg_ms * 1e-3) / 1e9,
+             "frac_of_peak": algo_bytes / (avg_ms * 1e-3) / 1e9 / PEAK_GBS,
+             "wall_ms_per_step": wall / steps * 1e3}
+        if note:
+            r["note"] = note
+        results[name] = r
+        return r
+
+    # ---------------- headline: bf16 [8192, 8192] exclusive row scan ----------------
+    head = None
+    rows, n = wl.FULL["rows_bf16"]
+    head_bytes = rows * n * 2 * 2
+    if want("rows_bf16_excl"):
+        xb = wl.rows_bf16(rows, n)
+        xs = [bf16_dev(xb) for _ in range(args.sets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
+        wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "add", True, ys[i % args.sets]),
+                          args.steps, args.warmup)
+        head = record("rows_bf16_excl", rows * n, head_bytes, wall, per, args.steps)
+        head["wall_s"] = wall
+        del xs, ys
+
+    # ---------------- the other workloads ----------------
+    K, W = args.sub_steps, 3
+    if want("rows_bf16_ragged_excl"):
+        r2, n2 = wl.FULL["rows_bf16_ragged"]
+        xb2 = wl.rows_bf16(r2, n2)
+        xs = [bf16_dev(xb2) for _ in range(args.sets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
+        wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "add", True, ys[i % args.sets]),
+                          K, W)
+        record("rows_bf16_ragged_excl", r2 * n2, r2 * n2 * 4, wall, per, K)
+        del xs, ys
+    r1, n1 = wl.FULL["rows_f32"]
+    for excl in (False, True):
+        name = "rows_f32_" + ("excl" if excl else "incl")
+        if not want(name):
+            continue
+        x1 = torch.from_numpy(wl.rows_f32(r1, n1)).to(dev)
+        sets = max(args.sets, 32)          # 32 MiB per set: rotate over >= 1 GiB
+        xs = [x1.clone() for _ in range(sets)]
+        ys = [torch.empty_like(x1) for _ in range(sets)]
+        wall, per = timed(lambda i: sc.scan_rows(xs[i % sets], "add", excl, ys[i % sets]), K, W)
+        record(name, r1 * n1, r1 * n1 * 8, wall, per, K)
+        del xs, ys
+    for name, n3 in (("dev_i32_add", wl.FULL["dev_i32"]), ("dev_i32_add_odd", wl.FULL["dev_i32_odd"])):
+        if not want(name):
+            continue
+        x3 = torch.from_numpy(wl.dev_i32()[:n3]).to(dev)
+        y3 = torch.empty_like(x3)
+        s3 = torch.empty(sc.scan_device_scratch_bytes(n3, "i32"), dtype=torch.uint8, device=dev)
+        wall, per = timed(lambda i: sc.scan_device(x3, "add", y3, s3), K, W)
+        record(name, n3, n3 * 8, wall, per, K, "includes the descriptor-reset fill kernel")
+        del x3, y3
+    for which in ("f32", "i64"):
+        if not any(want(f"dev_{which}_{op}") for op in ("min", "max")):
+            continue
+        x4 = torch.from_numpy(wl.dev_f32() if which == "f32" else wl.dev_i64()).to(dev)
+        y4 = torch.empty_like(x4)
+        s4 = torch.empty(sc.scan_device_scratch_bytes(x4.numel(), which), dtype=torch.uint8,
+                         device=dev)
+        for op in ("min", "max"):
+            name = f"dev_{which}_{op}"
+            if want(name):
+                wall, per = timed(lambda i: sc.scan_device(x4, op, y4, s4), K, W)
+                record(name, x4.numel(), x4.numel() * x4.element_size() * 2, wall, per, K,
+                       "includes the descriptor-reset fill kernel")
+        del x4, y4
+    nsel = wl.FULL["sel"]
+    for p in wl.SELECT_P:
+        name = f"select_p{p}"
+        if not want(name):
+            continue
+        pay, fl = wl.sel_inputs(nsel, p)
+        xp = torch.from_numpy(pay).to(dev)
+        xf = torch.from_numpy(fl).to(dev)
+        yo = torch.empty_like(xp)
+        num = torch.empty(1, dtype=torch.int32, device=dev)
+        ss = torch.empty(sc.select_compact_scratch_bytes(nsel), dtype=torch.uint8, device=dev)
+        wall, per = timed(lambda i: sc.select_compact(xp, xf, yo, num, ss), K, W)
+        k = int(num.item())
+        r = record(name, nsel, nsel * 5 + 4 * k + 4, wall, per, K,
+                   "algorithmic bytes = 4n payload + n flags read, 4k written, 4 count")
+        r["kept"] = k
+        r["read_n_plus_write_n_GBps"] = nsel * 8 / (r["kernel_ms_avg"] * 1e-3) / 1e9
+        del xp, xf, yo
+
+    # ---------------- copy ceiling over the headline's bytes ----------------
+    copy = None
+    if want("copy16"):
+        import ctypes
+        from stream_compaction_amd import build as _b
+        cl = ctypes.CDLL(_b.COPY_LIB_PATH)
+        cl.copy_ceiling_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p]
+        half = head_bytes // 2
+        srcs = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(args.sets)]
+        dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(args.sets)]
+
+        def cp(i):
+            rc = cl.copy_ceiling_copy16(ctypes.c_void_p(srcs[i % args.sets].data_ptr()),
+                                        ctypes.c_void_p(dsts[i % args.sets].data_ptr()), half,
+                                        ctypes.c_void_p(stream.cuda_stream))
+            assert rc == 0, rc
+        wall, per = timed(cp, args.steps, args.warmup)
+        copy = record("copy16", half // 2, head_bytes, wall, per, args.steps,
+                      "16-byte copy kernel moving the headline's read+write bytes")
+        del srcs, dsts
+
+    # ---------------- CPU oracle baseline on the headline workload ----------------
+    cpu = None
+    if not args.no_cpu and head is not None:
+        from concurrent.futures import ThreadPoolExecutor
+
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        blocks = np.array_split(np.arange(rows), threads)
+
+        def run_block(b):
+            oracle.scan(xb[b[0]:b[-1] + 1], "bf16", "add", exclusive=True)
+
+        times = []
+        with ThreadPoolExecutor(threads) as ex:
+            for _ in range(3):
+                t0 = time.perf_counter()
+                list(ex.map(run_block, blocks))
+                times.append(time.perf_counter() - t0)
+        t = float(np.median(times))
+        cpu = {"value": rows * n / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
+               "sample": f"the full workload, bf16 [{rows}, {n}] exclusive add, rows split "
+                         f"over {threads} threads, median of 3 runs ({t:.3f} s each)",
+               "cpu": platform.processor() or platform.machine()}
+
+    # ---------------- stored counter readings -> HBM traffic per launch ----------------
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        try:
+            pm = json.load(open(PMC_FILE))
+            k = pm["kernels"].get("rows_bf16_excl")
+            c = pm["copy16"]
+            if k and k.get("source_sha") == sources_sha("scan_rows"):
+                fr = c["bytes"] / 2 / (c["fetch_kib"] * 1024)     # bytes per counted byte
+                fw = c["bytes"] / 2 / (c["write_kib"] * 1024)
+                traffic = k["fetch_kib"] * 1024 * fr + k["write_kib"] * 1024 * fw
+        except (KeyError, ValueError, ZeroDivisionError):
+            traffic = None
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": (rows * n * args.steps / head["wall_s"]) if head else None,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (head["wall_s"] / args.steps * 1e3) if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "row-wise exclusive add scan along the last axis, bf16 "
+                               "[8192, 8192] N(0,1) seed 1, float32 accumulation, bf16 output "
+                               "rounded nearest-even",
+                   "rows": rows, "n": n, "io_dtype": "bf16", "accumulate": "f32",
+                   "buffer_sets": args.sets},
+    }
+    if head:
+        achieved = head_bytes / (head["kernel_ms_avg"] * 1e-3) / 1e9
+        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                            "traffic": traffic, "kernel": "scan_rows_kernel<bf16, add, excl>",
+                            "bytes_per_launch": head_bytes}
+        if copy:
+            line["roofline"]["copy16_GBps"] = round(copy["GBps"], 1)
+            line["roofline"]["frac_of_copy16"] = round(achieved / copy["GBps"], 4)
+    line["cpu_baseline"] = cpu
+    line["workloads"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                             for kk, vv in v.items() if kk != "wall_s"}
+                         for k, v in results.items()}
+    line["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                      "hbm_GiB": round(props.total_memory / 2**30, 1),
+                      "l2_bytes": getattr(props, "L2_cache_size", None),
+                      "torch": torch.__version__, "hip": torch.version.hip}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

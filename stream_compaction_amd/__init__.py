@@ -41,27 +41,32 @@ def lib():
     """Load libscan_amd.so (built in-tree by ``python -m stream_compaction_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m stream_compaction_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
-        L.scan_rows.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp]
-        L.scan_rows.restype = i32
-        L.scan_device_scratch_bytes.argtypes = [i64, i32]
-        L.scan_device_scratch_bytes.restype = sz
-        L.scan_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
-        L.scan_device.restype = i32
-        L.select_compact_scratch_bytes.argtypes = [i64]
-        L.select_compact_scratch_bytes.restype = sz
-        L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
-        L.select_compact.restype = i32
-        L.scan_status_str.argtypes = [i32]
-        L.scan_status_str.restype = ctypes.c_char_p
-        L.scan_last_hip_error.argtypes = []
-        L.scan_last_hip_error.restype = i32
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path):
+    """Load a build of the library at ``path`` and declare its C signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m stream_compaction_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.scan_rows.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp]
+    L.scan_rows.restype = i32
+    L.scan_device_scratch_bytes.argtypes = [i64, i32]
+    L.scan_device_scratch_bytes.restype = sz
+    L.scan_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
+    L.scan_device.restype = i32
+    L.select_compact_scratch_bytes.argtypes = [i64]
+    L.select_compact_scratch_bytes.restype = sz
+    L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
+    L.select_compact.restype = i32
+    L.scan_status_str.argtypes = [i32]
+    L.scan_status_str.restype = ctypes.c_char_p
+    L.scan_last_hip_error.argtypes = []
+    L.scan_last_hip_error.restype = i32
+    return L
 
 
 def check(status):

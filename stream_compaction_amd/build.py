@@ -15,6 +15,14 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libscan_amd.so")
 SOURCES = ["scan_rows.hip", "scan_device.hip", "select.hip", "api.cpp"]
+# measurement aid for the benchmark (16-byte copy kernel), kept out of the scan library
+COPY_LIB_PATH = os.path.join(HERE, "libscan_copy.so")
+COPY_SOURCES = ["copy_ceiling.hip"]
+# test-only build of the scan library whose look-back never waits: any
+# predecessor descriptor not yet published is recomputed from the input at
+# once, so the tests exercise that recovery path on every call
+FALLBACK_LIB_PATH = os.path.join(HERE, "libscan_amd_lbtest.so")
+FALLBACK_DEFINES = ["-DSCA_LOOKBACK_TIMEOUT_TICKS=0ull"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,19 +35,22 @@ CFLAGS = [
 ]
 
 
-def compile_cmd(src, obj):
+def compile_cmd(src, obj, defines=()):
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    return [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    return [HIPCC, *CFLAGS, *defines, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
 
 
 def build(verbose=False):
     os.makedirs(OBJ_DIR, exist_ok=True)
     procs = []
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
-        cmd = compile_cmd(src, obj)
+    libs = {LIB_PATH: [], COPY_LIB_PATH: [], FALLBACK_LIB_PATH: []}
+    jobs = [(LIB_PATH, s, ()) for s in SOURCES] + [(COPY_LIB_PATH, s, ()) for s in COPY_SOURCES] + \
+        [(FALLBACK_LIB_PATH, s, FALLBACK_DEFINES) for s in SOURCES]
+    for lib, src, defines in jobs:
+        tag = "_lbtest" if defines else ""
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + tag + ".o")
+        libs[lib].append(obj)
+        cmd = compile_cmd(src, obj, defines)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -55,10 +66,11 @@ def build(verbose=False):
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB_PATH + ".tmp"
-    subprocess.check_call([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
-                           "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    for path, lib_objs in libs.items():
+        tmp = path + ".tmp"
+        subprocess.check_call([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *lib_objs,
+                               "-o", tmp])
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -93,8 +93,7 @@ size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype) {
   sca::Fmt fmt;
   size_t eb;
   if (!fmt_of(dtype, &fmt, &eb) || n < 0) return 0;
-  return sca::kScratchHeader +
-         round16(sca::scan_device_tiles(n, fmt) * sca::scan_device_desc_words(fmt) * 8);
+  return round16(sca::scan_device_tiles(n, fmt) * sca::scan_device_desc_words(fmt) * 8);
 }
 
 scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
@@ -119,7 +118,7 @@ scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, 
 
 size_t select_compact_scratch_bytes(int64_t n) {
   if (n < 0) return 0;
-  return sca::kScratchHeader + round16(sca::select_tiles(n, 8) * 8);
+  return round16(sca::select_tiles(n, 8) * 8);
 }
 
 scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,

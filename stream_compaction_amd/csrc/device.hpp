@@ -198,43 +198,70 @@ __device__ __forceinline__ W wave_shift_excl(W incl) {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
-__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+// Wave index within the workgroup, as a wave-uniform (scalar) value so that
+// addresses and buffer resources derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
 
 // ---------------------------------------------------------------------------
 // Window addressing.  Kernels address an array through a 16-byte-aligned base
 // `abase` that lies `ph` elements before the array's first element; window
 // element index i is array element i - ph.  Vector v of the window covers
 // window elements [v*E, v*E + E) and is a naturally aligned 16-byte block
-// (E = 16 / sizeof(S)).  A vector lying entirely inside the valid range
-// [lo, hi) moves with one 16-byte load/store; a partial vector (ragged row
-// ends, array ends) moves element by element, touching only valid elements.
-// With E == 1 (arrays whose phases differ) every access is one element.
+// (E = 16 / sizeof(S)); with E == 1 (arrays whose phases differ) a vector is
+// one element.
+//
+// Loads go through a buffer resource whose range ends at the last vector that
+// holds a valid element, so every load is issued unconditionally (no branch,
+// hence no wait for one load before the next is issued) and a vector past the
+// range reads as zero bits without touching memory.  The vectors at the two
+// ends of a valid range may hold neighbouring elements: they are masked to
+// the identity after the load (only the two end vectors of a range are
+// partial, and a 16-byte block never straddles a page, so reading them is
+// safe).  Full vectors are stored with one 16-byte nontemporal store; partial
+// vectors element by element, touching only valid elements.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A global-memory (address space 1) pointer to T at integer address a.  Going
+// through it, rather than a generic pointer, makes the compiler emit global_*
+// instead of flat_* instructions, whose extra counter use would force waits.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr(uintptr_t a) {
+  return (__attribute__((address_space(1))) T*)a;
+}
+
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  // [base, base + bytes): base must be wave-uniform; bytes is clamped to the
+  // 32-bit range of a buffer resource (callers keep windows below 2 GiB).
+  __device__ __forceinline__ Buf(uintptr_t base, int64_t bytes) {
+    const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7ffffff0 ? 0x7ffffff0 : (int)bytes);
+    r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
+  }
+};
+
+constexpr int kNT = 2;  // nontemporal cache policy for streaming loads
+
 template <class S, int E>
 struct VecIO {
   static_assert(E == 1 || E * sizeof(S) == 16, "a vector is one element or 16 bytes");
   // Raw storage bits of one vector.
   using Raw = std::conditional_t<E == 1, S, uint4>;
 
-  static __device__ __forceinline__ S at(uintptr_t abase, int64_t i) {
-    return *(const S*)(abase + i * sizeof(S));
-  }
-
-  // Storage bits of vector v; elements outside [lo, hi) read as `fill`.
-  static __device__ __forceinline__ Raw load(uintptr_t abase, int64_t v, int64_t lo, int64_t hi,
-                                             S fill) {
-    const int64_t e0 = v * E;
+  // Vector at byte offset `off` of buffer b (zero bits when out of its range).
+  static __device__ __forceinline__ Raw load(const Buf& b, uint32_t off) {
     if constexpr (E == 1) {
-      return (e0 >= lo && e0 < hi) ? at(abase, e0) : fill;
-    } else {
-      if (e0 >= lo && e0 + E <= hi) return *(const uint4*)(abase + e0 * sizeof(S));
-      S e[E];
-#pragma unroll
-      for (int k = 0; k < E; ++k) {
-        const int64_t i = e0 + k;
-        e[k] = (i >= lo && i < hi) ? at(abase, i) : fill;
+      if constexpr (sizeof(S) == 2) {
+        return __builtin_bit_cast(S, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, kNT));
+      } else if constexpr (sizeof(S) == 4) {
+        return __builtin_bit_cast(S, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, kNT));
+      } else {
+        return __builtin_bit_cast(S, __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, kNT));
       }
-      return __builtin_bit_cast(uint4, e);
+    } else {
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, kNT));
     }
   }
 
@@ -258,6 +285,16 @@ struct VecIO {
         x[1] = widen<F>(__builtin_bit_cast(S, ((uint64_t)d[3] << 32) | d[2]));
       }
     }
+  }
+
+  // unpack, with elements outside window range [lo, hi) replaced by `id`
+  template <class F>
+  static __device__ __forceinline__ void unpack_masked(const Raw r, int64_t e0, int64_t lo,
+                                                       int64_t hi, typename F::W id,
+                                                       typename F::W (&x)[E]) {
+    unpack<F>(r, x);
+#pragma unroll
+    for (int k = 0; k < E; ++k) x[k] = (e0 + k >= lo && e0 + k < hi) ? x[k] : id;
   }
 
   template <class F>
@@ -284,15 +321,16 @@ struct VecIO {
                                                const typename F::W (&y)[E]) {
     const int64_t e0 = v * E;
     if constexpr (E == 1) {
-      if (e0 >= lo && e0 < hi) *(S*)(abase + e0 * sizeof(S)) = narrow<F>(y[0]);
+      if (e0 >= lo && e0 < hi) *gptr<S>(abase + e0 * sizeof(S)) = narrow<F>(y[0]);
     } else {
       if (e0 >= lo && e0 + E <= hi) {
-        *(uint4*)(abase + e0 * sizeof(S)) = pack<F>(y);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pack<F>(y)),
+                                    gptr<u32x4>(abase + e0 * sizeof(S)));
       } else {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
           const int64_t i = e0 + k;
-          if (i >= lo && i < hi) *(S*)(abase + i * sizeof(S)) = narrow<F>(y[k]);
+          if (i >= lo && i < hi) *gptr<S>(abase + i * sizeof(S)) = narrow<F>(y[k]);
         }
       }
     }
@@ -368,22 +406,46 @@ template <class W> struct Desc<W, 8> {
 // [nearest inclusive .. 63] in order with the wave scan, and prepends the
 // result to what later windows already gave.  Tiles before 0 read as
 // inclusive identities, so the walk always ends.
-template <Op O, class W>
-__device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile) {
+//
+// Waiting is bounded.  If a window's descriptors are not all published within
+// `timeout` ticks of the 100 MHz real-time counter, the wave computes each
+// missing tile's aggregate itself with reduce_tile(t) (a wave-cooperative
+// reduction of tile t's input returning a wave-uniform value; the input never
+// changes, so this is exactly what that tile would publish).  The walk then
+// needs nothing from workgroups that have not started, so it ends whatever
+// order the hardware runs workgroups in; in the usual case no descriptor is
+// that late and no tile is reduced twice.
+template <Op O, class W, class ReduceTile>
+__device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint64_t timeout,
+                                       ReduceTile&& reduce_tile) {
   const int lane = lane_id();
   const W id = identity<O, W>();
   W prefix = id;
   for (int64_t base = tile - 1;; base -= kWave) {
     const int64_t t = base - (kWave - 1) + lane;
     W v = id;
-    uint32_t st;
+    uint32_t st = kNone;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (;;) {
       st = (t < 0) ? (uint32_t)kInc : Desc<W>::read(desc, t, v);
       if (t < 0) v = id;
       const uint64_t inc = __ballot(st == kInc);
       const uint64_t none = __ballot(st == kNone);
       const uint64_t need = inc ? (~0ull << (63 - __builtin_clzll(inc))) : ~0ull;
-      if ((none & need) == 0) break;
+      uint64_t pending = none & need;
+      if (pending == 0) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > timeout) {
+        while (pending) {                       // nearest missing tile first
+          const int l = 63 - __builtin_clzll(pending);
+          const W a = reduce_tile(base - (kWave - 1) + l);
+          if (lane == l) {
+            v = a;
+            st = kAgg;
+          }
+          pending &= ~(1ull << l);
+        }
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     const uint64_t inc = __ballot(st == kInc);
@@ -394,5 +456,14 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile) {
     if (inc) return prefix;
   }
 }
+
+// Wait bound of the look-back before it reduces a late predecessor itself,
+// in ticks of the 100 MHz real-time counter.  Far above the latency of a
+// published descriptor (microseconds), so in practice it only matters if a
+// predecessor's workgroup has not been scheduled.
+#ifndef SCA_LOOKBACK_TIMEOUT_TICKS
+#define SCA_LOOKBACK_TIMEOUT_TICKS 20000ull  // 200 us
+#endif
+constexpr uint64_t kLookBackTimeout = SCA_LOOKBACK_TIMEOUT_TICKS;
 
 }  // namespace sca

@@ -29,10 +29,8 @@ size_t select_tiles(int64_t n, size_t elem_bytes);
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                          int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream);
 
-// Scratch layout shared by the look-back kernels: a 256-byte header whose
-// first dword is the dynamic tile counter, then the descriptor words.
-constexpr size_t kScratchHeader = 256;
-
+// Scratch of the look-back kernels holds only the tile descriptor words
+// (zeroed at the start of every call).
 // Zero `bytes` rounded up to a multiple of 16 at a 16-byte-aligned device
 // address (scratch sizes are rounded the same way) with a small fill kernel
 // (no hipMemsetAsync, so the call can sit in a captured graph).

@@ -3,75 +3,76 @@
 // qd.algorithms.exclusive_scan_{add,min,max} for the contract, "Related" for
 // decoupled look-back as the alternative to a phase-per-launch staircase).
 //
-// Each 256-thread workgroup takes the next tile id from an atomic counter (so
-// every tile it may wait on belongs to a workgroup that is already running),
-// loads its tile as 16-byte vectors (load j of lane l is vector j*64 + l of
-// its wave's segment), and:
+// Workgroup b owns tile b (WPB waves, K 16-byte vectors per lane).  It loads
+// its tile (load j of lane l in wave w is vector (w*K + j)*64 + l of the
+// tile, so every load instruction covers 1 KiB of contiguous memory) and:
 //   1. scans every vector lane-serially, then the 64 lane totals with a DPP
 //      wave scan, keeping per vector the combine of everything before it in
 //      the wave;
-//   2. publishes the four wave totals through LDS; wave 0 forms the tile
+//   2. publishes the wave totals through LDS; wave 0 forms the tile
 //      aggregate, publishes it, looks back over predecessor descriptors to
 //      get the tile's exclusive prefix, and publishes its inclusive prefix;
 //   3. after one more barrier every lane combines tile prefix, earlier waves,
 //      earlier vectors and earlier elements of its vector, and stores.
-// The input is read once and the output written once.
+// The input is read once and the output written once.  Tile ids are the
+// workgroup ids: no atomic counter (a device-wide atomic on one address
+// serializes at about 11 ns per tile on MI355X); the look-back's bounded wait
+// (device.hpp) keeps this correct and deadlock-free under any workgroup order.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace sca {
 
-constexpr int kDevK = 16;                                  // vectors per lane per tile
-constexpr int64_t kDevTileVecs = (int64_t)kBlock * kDevK;  // vectors per tile
+// Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
+constexpr int64_t kDevMinTileVecs = 1024;
 
-template <class F, Op O, int E, int K>
-__global__ __launch_bounds__(256) void scan_device_kernel(uintptr_t in_base, uintptr_t out_base,
-                                                         int64_t n, int64_t ph, int64_t ntiles,
-                                                         uint32_t* counter, uint64_t* desc) {
+template <class F, Op O, int E, int WPB, int K>
+__global__ __launch_bounds__(64 * WPB) void scan_device_kernel(uintptr_t in_base, uintptr_t out_base,
+                                                              int64_t n, int64_t ph, int64_t ntiles,
+                                                              uint64_t* desc) {
   using S = typename F::S;
   using W = typename F::W;
   using IO = VecIO<S, E>;
-  constexpr int64_t kTileVecs = (int64_t)kBlock * K;
-  __shared__ W s_wave[kBlock / kWave];
+  constexpr int64_t VB = (int64_t)E * sizeof(S);       // bytes per vector
+  constexpr int64_t kWaveVecs = (int64_t)kWave * K;
+  constexpr int64_t kTileVecs = kWaveVecs * WPB;
+  static_assert(kTileVecs >= kDevMinTileVecs, "scratch is sized for the smallest tile");
+  __shared__ W s_wave[WPB];
   __shared__ W s_prefix;
-  __shared__ int64_t s_tile;
 
   const int lane = lane_id(), wave = wave_id();
-  if (threadIdx.x == 0)
-    s_tile = (int64_t)__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int64_t tile = s_tile;
-  if (tile >= ntiles) return;
-
+  const int64_t tile = blockIdx.x;
   const W id = identity<O, W>();
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
-  const int64_t vb = tile * kTileVecs + (int64_t)wave * kWave * K;
 
-  typename IO::Raw raw[K];
-  const S id_s = narrow<F>(id);
+  // A wave's K loads of the run of 64*K vectors starting at `first` (zero bits past v_last).
+  auto load = [&](int64_t first, typename IO::Raw (&raw)[K]) {
+    const int64_t left = v_last + 1 - first;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf buf(in_base + first * VB, nv * VB);
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int64_t v = vb + j * kWave + lane;
-    raw[j] = (v <= v_last) ? IO::load(in_base, v, lo, hi, id_s) : typename IO::Raw{};
-  }
-  W x[K][E];
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int64_t v = vb + j * kWave + lane;
-    if (v <= v_last) {
-      IO::template unpack<F>(raw[j], x[j]);
+    for (int j = 0; j < K; ++j) raw[j] = IO::load(buf, (uint32_t)((j * kWave + lane) * VB));
+  };
+  // Elements of load j (first vector of the load: jv) with the identity outside [lo, hi).
+  auto unpack = [&](int64_t jv, const typename IO::Raw& r, W (&x)[E]) {
+    if (jv * E >= lo && (jv + kWave) * E <= hi) {       // wave-uniform: all vectors full
+      IO::template unpack<F>(r, x);
     } else {
-#pragma unroll
-      for (int k = 0; k < E; ++k) x[j][k] = id;
+      IO::template unpack_masked<F>(r, (jv + lane) * E, lo, hi, id, x);
     }
-  }
+  };
+
+  const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
+  typename IO::Raw raw[K];
+  load(wb, raw);
 
   // 1. within the wave
+  W x[K][E];
   W pre[K];
   W carry = id;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
+    unpack(wb + j * kWave, raw[j], x[j]);
 #pragma unroll
     for (int k = 1; k < E; ++k) x[j][k] = combine<O>(x[j][k - 1], x[j][k]);
     const W incl = wave_scan_incl<O>(x[j][E - 1]);
@@ -85,13 +86,31 @@ __global__ __launch_bounds__(256) void scan_device_kernel(uintptr_t in_base, uin
   if (wave == 0) {
     W agg = s_wave[0];
 #pragma unroll
-    for (int w = 1; w < kBlock / kWave; ++w) agg = combine<O>(agg, s_wave[w]);
+    for (int w = 1; w < WPB; ++w) agg = combine<O>(agg, s_wave[w]);
     W prefix = id;
     if (tile == 0) {
       if (lane == 0) Desc<W>::publish(desc, tile, kInc, agg);
     } else {
       if (lane == 0) Desc<W>::publish(desc, tile, kAgg, agg);
-      prefix = look_back<O, W>(desc, tile);
+      // fallback for a late predecessor: reduce its input in element order
+      auto reduce_tile = [&](int64_t t) -> W {
+        W acc = id;
+        for (int c = 0; c < WPB; ++c) {
+          typename IO::Raw r[K];
+          const int64_t first = t * kTileVecs + c * kWaveVecs;
+          load(first, r);
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            W y[E];
+            unpack(first + j * kWave, r[j], y);
+#pragma unroll
+            for (int k = 1; k < E; ++k) y[k] = combine<O>(y[k - 1], y[k]);
+            acc = combine<O>(acc, readlane(wave_scan_incl<O>(y[E - 1]), kWave - 1));
+          }
+        }
+        return acc;
+      };
+      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile);
       if (lane == 0) Desc<W>::publish(desc, tile, kInc, combine<O>(prefix, agg));
     }
     if (lane == 0) s_prefix = prefix;
@@ -108,16 +127,17 @@ __global__ __launch_bounds__(256) void scan_device_kernel(uintptr_t in_base, uin
     y[0] = q;
 #pragma unroll
     for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
-    const int64_t v = vb + j * kWave + lane;
+    const int64_t v = wb + j * kWave + lane;
     if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
   }
 }
 
-// Tiles covering window elements [ph, n + ph) (ph < e) in vectors of e elements.
-static int64_t tiles_for(int64_t n, int e) {
+// Tiles of tv vectors covering window elements [ph, n + ph) (ph < e) in
+// vectors of e elements.
+static int64_t tiles_for(int64_t n, int e, int64_t tv) {
   if (n <= 0) return 0;
   const int64_t v_last = (n - 1 + (e - 1)) / e;
-  return v_last / kDevTileVecs + 1;
+  return v_last / tv + 1;
 }
 
 static int fmt_bytes(Fmt f) {
@@ -130,37 +150,43 @@ static int fmt_bytes(Fmt f) {
 
 size_t scan_device_desc_words(Fmt fmt) { return fmt_bytes(fmt) == 8 ? 4 : 1; }
 
-// Sized for the slowest path (one element per vector) so one scratch size
-// serves every pointer alignment.
+// Sized for the slowest path (one element per vector) and the smallest tile,
+// so one scratch size serves every pointer alignment and launch shape.
 size_t scan_device_tiles(int64_t n, Fmt fmt) {
   (void)fmt;
-  return (size_t)tiles_for(n, 1);
+  return (size_t)tiles_for(n, 1, kDevMinTileVecs);
+}
+
+// One launch shape: WPB waves per workgroup, K vectors per lane per tile.
+template <class F, Op O, int WPB, int K>
+static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
+                                 hipStream_t stream) {
+  using S = typename F::S;
+  constexpr int EV = 16 / (int)sizeof(S);
+  constexpr int64_t TV = (int64_t)kWave * WPB * K;
+  const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
+  uint64_t* desc = (uint64_t*)scratch;
+  const bool vec = (ia % 16) == (oa % 16);
+  const int e = vec ? EV : 1;
+  const int64_t ph = vec ? (int64_t)((ia % 16) / sizeof(S)) : 0;
+  const int64_t ntiles = tiles_for(n, e, TV);
+  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * Desc<typename F::W>::kWords * 8,
+                                    stream);
+  if (err != hipSuccess) return err;
+  const dim3 grid((unsigned)ntiles), block(64 * WPB);
+  if (vec) {
+    scan_device_kernel<F, O, EV, WPB, K><<<grid, block, 0, stream>>>(
+        ia - ph * sizeof(S), oa - ph * sizeof(S), n, ph, ntiles, desc);
+  } else {
+    scan_device_kernel<F, O, 1, WPB, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles, desc);
+  }
+  return hipGetLastError();
 }
 
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, void* scratch,
                                hipStream_t stream) {
-  using S = typename F::S;
-  constexpr int EV = 16 / (int)sizeof(S);
-  const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
-  uint32_t* counter = (uint32_t*)scratch;
-  uint64_t* desc = (uint64_t*)((char*)scratch + kScratchHeader);
-  const bool vec = (ia % 16) == (oa % 16);
-  const int e = vec ? EV : 1;
-  const int64_t ph = vec ? (int64_t)((ia % 16) / sizeof(S)) : 0;
-  const int64_t ntiles = tiles_for(n, e);
-  hipError_t err = launch_fill_zero(
-      scratch, kScratchHeader + (size_t)ntiles * Desc<typename F::W>::kWords * 8, stream);
-  if (err != hipSuccess) return err;
-  const dim3 grid((unsigned)ntiles), block(kBlock);
-  if (vec) {
-    scan_device_kernel<F, O, EV, kDevK><<<grid, block, 0, stream>>>(
-        ia - ph * sizeof(S), oa - ph * sizeof(S), n, ph, ntiles, counter, desc);
-  } else {
-    scan_device_kernel<F, O, 1, kDevK><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles, counter,
-                                                                    desc);
-  }
-  return hipGetLastError();
+  return launch_dev_cfg<F, O, 4, 16>(in, out, n, scratch, stream);
 }
 
 template <class F>

@@ -2,95 +2,139 @@
 // [rows, n] array (metaltile-std src/mlx/scan.rs: header comment for the
 // definitions, "Multi-op scan variants" for min/max and their identities).
 //
-// Mapping: one wave64 owns one row; a 256-thread workgroup holds four rows.
-// A row is read as consecutive 16-byte vectors of a window aligned to 16
-// bytes (so ragged rows, whose starts are not 16-byte aligned, still move in
-// full vectors except at their two ends).  Per chunk of 64*K vectors the wave
-// issues all K loads first (load j of lane l is vector j*64 + l, so every
-// load instruction covers 1 KiB of contiguous memory), then per load:
-//   1. each lane scans its E elements serially in the accumulation type
-//      (float32 for every float input, as the page's kernels cast each load);
-//   2. the 64 lane totals are scanned across the wave with DPP
-//      (wave_scan_incl), then shifted one lane for the exclusive offsets;
-//   3. the running row prefix (`carry`, wave-uniform) is combined in front;
-//   4. outputs are formed as prefix (+) lane-local prefix, with the exclusive
+// Mapping: one workgroup of WPR wave64s owns one row and walks it in chunks of
+// WPR*64*K vectors of a 16-byte-aligned window (so ragged rows, whose starts
+// are not 16-byte aligned, still move in full vectors except at their two
+// ends).  Wave w takes the w-th run of 64*K vectors of a chunk, and load j of
+// its lane l is vector j*64 + l of that run, so every load instruction covers
+// 1 KiB of contiguous memory.  Per chunk:
+//   1. every wave issues its K loads (unconditionally; past the row they read
+//      zeros), then per load: each lane scans its E elements serially in the
+//      accumulation type (float32 for every float input, as the page's kernels
+//      cast each load), the 64 lane totals are scanned across the wave with
+//      DPP, and the running wave total is carried from load to load;
+//   2. wave totals meet in LDS (one barrier per chunk; double-buffered so the
+//      next chunk needs no second barrier), giving each wave the combine of
+//      the row before it;
+//   3. outputs are formed as prefix (+) lane-local prefix, the exclusive
 //      variant reading the lane-local prefix one slot earlier (the "one-slot
 //      store shift" of that page), narrowed with round-to-nearest-even and
 //      stored with the same vector layout.
-// No LDS and no barrier: the rows of a workgroup are independent.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace sca {
 
-template <class F, Op O, bool EXCL, int E, int K>
-__global__ __launch_bounds__(256) void scan_rows_kernel(uintptr_t in_base, uintptr_t out_base,
-                                                       int64_t rows, int64_t n, int64_t ph) {
+template <class F, Op O, bool EXCL, int E, int WPR, int K>
+__global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, uintptr_t out_base,
+                                                            int64_t rows, int64_t n, int64_t ph) {
   using S = typename F::S;
   using W = typename F::W;
   using IO = VecIO<S, E>;
-  const int lane = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-  if (row >= rows) return;
+  constexpr int64_t VB = (int64_t)E * sizeof(S);       // bytes per vector
+  constexpr int64_t kWaveVecs = (int64_t)kWave * K;     // vectors per wave per chunk
+  constexpr int64_t kChunkVecs = kWaveVecs * WPR;       // vectors per chunk
+  __shared__ W s_tot[2][WPR];
+
+  const int lane = lane_id(), wave = wave_id();
+  const int64_t row = blockIdx.x;
   // valid window elements of this row, and the vectors that cover them
   const int64_t lo = row * n + ph, hi = lo + n;
   const int64_t v_first = lo / E, v_last = (hi - 1) / E;
   const W id = identity<O, W>();
-  const S id_s = narrow<F>(id);
-  W carry = id;
-  for (int64_t vb = v_first; vb <= v_last; vb += (int64_t)kWave * K) {
-    // all loads of the chunk first, kept as raw storage bits
+  W carry = id;  // combine of the row before the current chunk
+  int parity = 0;
+  for (int64_t vb = v_first; vb <= v_last; vb += kChunkVecs) {
+    const int64_t wb = vb + wave * kWaveVecs;           // this wave's first vector
+    const int64_t left = v_last + 1 - wb;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf buf(in_base + wb * VB, nv * VB);
     typename IO::Raw raw[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int64_t v = vb + j * kWave + lane;
-      if (v <= v_last) raw[j] = IO::load(in_base, v, lo, hi, id_s);
-    }
+    for (int j = 0; j < K; ++j) raw[j] = IO::load(buf, (uint32_t)((j * kWave + lane) * VB));
+
+    // 1. within the wave: x[j] becomes the lane-local inclusive prefix and
+    //    pre[j] the combine of the wave's elements before the lane's vector
+    W x[K][E];
+    W pre[K];
+    W wtot = id;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t v = vb + j * kWave + lane;
-      W x[E];
-      if (v <= v_last) {
-        IO::template unpack<F>(raw[j], x);
+      const int64_t jv = wb + j * kWave;
+      if (jv * E >= lo && (jv + kWave) * E <= hi) {     // wave-uniform: all vectors full
+        IO::template unpack<F>(raw[j], x[j]);
       } else {
-#pragma unroll
-        for (int k = 0; k < E; ++k) x[k] = id;
+        IO::template unpack_masked<F>(raw[j], (jv + lane) * E, lo, hi, id, x[j]);
       }
-      // 1. lane-serial inclusive prefix, in place
 #pragma unroll
-      for (int k = 1; k < E; ++k) x[k] = combine<O>(x[k - 1], x[k]);
-      // 2. across the wave
-      const W incl = wave_scan_incl<O>(x[E - 1]);
-      const W excl = wave_shift_excl<O>(incl);
-      // 3. everything before this lane's vector
-      const W pre = combine<O>(carry, excl);
-      carry = combine<O>(carry, readlane(incl, kWave - 1));
-      // 4. outputs
+      for (int k = 1; k < E; ++k) x[j][k] = combine<O>(x[j][k - 1], x[j][k]);
+      const W incl = wave_scan_incl<O>(x[j][E - 1]);
+      pre[j] = combine<O>(wtot, wave_shift_excl<O>(incl));
+      wtot = combine<O>(wtot, readlane(incl, kWave - 1));
+    }
+
+    // 2. across the waves of the chunk
+    W wp = carry;
+    if constexpr (WPR > 1) {
+      if (lane == 0) s_tot[parity][wave] = wtot;
+      __syncthreads();
+      W all = carry;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) {
+        const W t = s_tot[parity][w];
+        if (w < wave) wp = combine<O>(wp, t);
+        all = combine<O>(all, t);
+      }
+      carry = all;
+      parity ^= 1;
+    } else {
+      carry = combine<O>(carry, wtot);
+    }
+
+    // 3. outputs
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const W q = combine<O>(wp, pre[j]);
       W y[E];
       if constexpr (EXCL) {
-        y[0] = pre;
+        y[0] = q;
 #pragma unroll
-        for (int k = 1; k < E; ++k) y[k] = combine<O>(pre, x[k - 1]);
+        for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
       } else {
 #pragma unroll
-        for (int k = 0; k < E; ++k) y[k] = combine<O>(pre, x[k]);
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(q, x[j][k]);
       }
+      const int64_t v = wb + j * kWave + lane;
       if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
     }
   }
 }
 
+template <class F, Op O, bool EXCL, int E, int WPR, int K>
+static void launch_rows_cfg(uintptr_t in_base, uintptr_t out_base, int64_t rows, int64_t n,
+                            int64_t ph, hipStream_t stream) {
+  scan_rows_kernel<F, O, EXCL, E, WPR, K><<<dim3((unsigned)rows), dim3(64 * WPR), 0, stream>>>(
+      in_base, out_base, rows, n, ph);
+}
+
+// Launch shape by the number of 16-byte vectors a row touches (measured on
+// MI355X for bf16 rows of 8192 / 8191 elements: four waves of four loads, or
+// five for a ragged row that straddles one more vector, beat both one long
+// wave per row and wide 16-wave groups).
 template <class F, Op O, bool EXCL, int E>
 static hipError_t launch_rows_e(uintptr_t in_base, uintptr_t out_base, int64_t rows, int64_t n,
                                 int64_t ph, hipStream_t stream) {
   const int64_t vmax = (n + 2 * E - 2) / E;  // vectors one row can touch
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (vmax <= kWave) {
-    scan_rows_kernel<F, O, EXCL, E, 1><<<grid, block, 0, stream>>>(in_base, out_base, rows, n, ph);
+    launch_rows_cfg<F, O, EXCL, E, 1, 1>(in_base, out_base, rows, n, ph, stream);
   } else if (vmax <= 4 * kWave) {
-    scan_rows_kernel<F, O, EXCL, E, 4><<<grid, block, 0, stream>>>(in_base, out_base, rows, n, ph);
+    launch_rows_cfg<F, O, EXCL, E, 2, 2>(in_base, out_base, rows, n, ph, stream);
+  } else if (vmax <= 16 * kWave) {
+    launch_rows_cfg<F, O, EXCL, E, 4, 4>(in_base, out_base, rows, n, ph, stream);
+  } else if (vmax <= 20 * kWave) {
+    launch_rows_cfg<F, O, EXCL, E, 4, 5>(in_base, out_base, rows, n, ph, stream);
   } else {
-    scan_rows_kernel<F, O, EXCL, E, 17><<<grid, block, 0, stream>>>(in_base, out_base, rows, n, ph);
+    launch_rows_cfg<F, O, EXCL, E, 8, 4>(in_base, out_base, rows, n, ph, stream);
   }
   return hipGetLastError();
 }

@@ -24,84 +24,105 @@
 
 namespace sca {
 
-constexpr int kSelK = 8;                                   // vectors per lane per tile
-constexpr int64_t kSelTileVecs = (int64_t)kBlock * kSelK;  // vectors per tile
+// Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
+constexpr int64_t kSelMinTileVecs = 1024;
 
 template <int EB> struct Bits;
 template <> struct Bits<4> { using T = uint32_t; };
 template <> struct Bits<8> { using T = uint64_t; };
 
-template <int EB, int E, bool FVEC, int K>
-__global__ __launch_bounds__(256) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
-                                                    uintptr_t out_base, int64_t n, int64_t ph,
-                                                    int64_t out_ph, int64_t ntiles,
-                                                    int32_t* num_out, uint32_t* counter,
-                                                    uint64_t* desc) {
+template <int EB, int E, bool FVEC, int WPB, int K>
+__global__ __launch_bounds__(64 * WPB) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
+                                                         uintptr_t out_base, int64_t n, int64_t ph,
+                                                         int64_t out_ph, int64_t ntiles,
+                                                         int32_t* num_out, uint64_t* desc) {
   using T = typename Bits<EB>::T;
   constexpr int EO = 16 / EB;                     // elements per 16-byte output vector
-  constexpr int64_t kTileVecs = (int64_t)kBlock * K;
+  constexpr int kThreads = kWave * WPB;
+  constexpr int64_t kWaveVecs = (int64_t)kWave * K;
+  constexpr int64_t kTileVecs = kWaveVecs * WPB;
+  static_assert(kTileVecs >= kSelMinTileVecs, "scratch is sized for the smallest tile");
   constexpr int kTileElems = (int)kTileVecs * E;
+  constexpr int64_t VB = (int64_t)E * EB;
   __shared__ __attribute__((aligned(16))) T s_stage[kTileElems + EO];
-  __shared__ uint32_t s_wave[kBlock / kWave];
+  __shared__ uint32_t s_wave[WPB];
   __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_tile;
 
   const int lane = lane_id(), wave = wave_id();
-  if (threadIdx.x == 0)
-    s_tile = (int64_t)__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int64_t tile = s_tile;
-  if (tile >= ntiles) return;
-
+  const int64_t tile = blockIdx.x;
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
-  const int64_t vb = tile * kTileVecs + (int64_t)wave * kWave * K;
 
-  // 1. payload and selection masks
-  T x[K][E];
-  uint32_t m[K];
+  // Flag bytes of the run of 64*K vectors starting at `first` (E bytes per
+  // vector, packed low byte first; zero past v_last).
+  auto load_flags = [&](int64_t first, uint32_t (&f)[K]) {
+    const int64_t left = v_last + 1 - first;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf fbuf(flags_base + first * E, nv * E);
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int64_t v = vb + j * kWave + lane;
-    m[j] = 0u;
-    if (v <= v_last) {
-      const int64_t e0 = v * E;
-      if (e0 >= lo && e0 + E <= hi) {
-        if constexpr (E == 1) {
-          x[j][0] = *(const T*)(in_base + e0 * EB);
-        } else {
-          const uint4 r = *(const uint4*)(in_base + e0 * EB);
-          if constexpr (EB == 4) {
-            x[j][0] = r.x; x[j][1] = r.y; x[j][2] = r.z; x[j][3] = r.w;
-          } else {
-            x[j][0] = ((uint64_t)r.y << 32) | r.x;
-            x[j][1] = ((uint64_t)r.w << 32) | r.z;
-          }
-        }
-        uint32_t f;
-        if constexpr (FVEC && E == 4) {
-          f = *(const uint32_t*)(flags_base + e0);
-        } else if constexpr (FVEC && E == 2) {
-          f = *(const uint16_t*)(flags_base + e0);
-        } else {
-          f = 0u;
-#pragma unroll
-          for (int k = 0; k < E; ++k) f |= (uint32_t)(*(const uint8_t*)(flags_base + e0 + k)) << (8 * k);
-        }
-#pragma unroll
-        for (int k = 0; k < E; ++k) m[j] |= (((f >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << k;
+    for (int j = 0; j < K; ++j) {
+      const uint32_t u = (uint32_t)(j * kWave + lane);
+      if constexpr (FVEC && E == 4) {
+        f[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(fbuf.r, u * 4, 0, kNT);
+      } else if constexpr (FVEC && E == 2) {
+        f[j] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(fbuf.r, u * 2, 0, kNT);
       } else {
+        f[j] = 0u;
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-          const int64_t i = e0 + k;
-          if (i >= lo && i < hi) {
-            x[j][k] = *(const T*)(in_base + i * EB);
-            m[j] |= (*(const uint8_t*)(flags_base + i) != 0 ? 1u : 0u) << k;
-          }
+        for (int k = 0; k < E; ++k)
+          f[j] |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(fbuf.r, u * E + k, 0, kNT)
+                  << (8 * k);
+      }
+    }
+  };
+  // Selection mask (bit k = element k) of the lane's vector in load j.
+  auto select_mask = [&](int64_t jv, uint32_t f) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int k = 0; k < E; ++k) m |= (((f >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << k;
+    if (!(jv * E >= lo && (jv + kWave) * E <= hi)) {   // wave-uniform: some vector is partial
+      const int64_t e0 = (jv + lane) * E;
+      const int64_t ks = lo - e0, ke = hi - e0;
+      const uint32_t start = ks <= 0 ? 0u : (ks >= E ? (uint32_t)E : (uint32_t)ks);
+      const uint32_t end = ke <= 0 ? 0u : (ke >= E ? (uint32_t)E : (uint32_t)ke);
+      m &= ((1u << end) - 1u) & ~((1u << start) - 1u);
+    }
+    return m;
+  };
+
+  // 1. payload and selection masks: every load is issued unconditionally through
+  //    buffer resources that end at the wave's last valid vector (past it: zero
+  //    bits, i.e. unselected); only the two end vectors of the array need masking
+  const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
+  T x[K][E];
+  uint32_t f[K];
+  {
+    const int64_t left = v_last + 1 - wb;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf pbuf(in_base + wb * VB, nv * VB);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t u = (uint32_t)(j * kWave + lane);
+      if constexpr (E == 1) {
+        if constexpr (EB == 4) {
+          x[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(pbuf.r, u * 4, 0, kNT);
+        } else {
+          x[j][0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(pbuf.r, u * 8, 0, kNT));
+        }
+      } else {
+        const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, u * 16, 0, kNT));
+        if constexpr (EB == 4) {
+          x[j][0] = r.x; x[j][1] = r.y; x[j][2] = r.z; x[j][3] = r.w;
+        } else {
+          x[j][0] = ((uint64_t)r.y << 32) | r.x;
+          x[j][1] = ((uint64_t)r.w << 32) | r.z;
         }
       }
     }
   }
+  load_flags(wb, f);
+  uint32_t m[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) m[j] = select_mask(wb + j * kWave, f[j]);
 
   // 2. ranks: within the wave, across waves, across tiles
   uint32_t pre[K];
@@ -117,13 +138,27 @@ __global__ __launch_bounds__(256) void select_kernel(uintptr_t in_base, uintptr_
   if (wave == 0) {
     uint32_t agg = 0u;
 #pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) agg += s_wave[w];
+    for (int w = 0; w < WPB; ++w) agg += s_wave[w];
     uint32_t prefix = 0u;
     if (tile == 0) {
       if (lane == 0) Desc<uint32_t>::publish(desc, tile, kInc, agg);
     } else {
       if (lane == 0) Desc<uint32_t>::publish(desc, tile, kAgg, agg);
-      prefix = look_back<Op::Add, uint32_t>(desc, tile);
+      // fallback for a late predecessor: count its selected flags
+      auto reduce_tile = [&](int64_t t) -> uint32_t {
+        uint32_t acc = 0u;
+        for (int c = 0; c < WPB; ++c) {
+          const int64_t first = t * kTileVecs + c * kWaveVecs;
+          uint32_t g[K];
+          load_flags(first, g);
+          uint32_t cnt = 0u;
+#pragma unroll
+          for (int j = 0; j < K; ++j) cnt += (uint32_t)__builtin_popcount(select_mask(first + j * kWave, g[j]));
+          acc += readlane(wave_scan_incl<Op::Add>(cnt), kWave - 1);
+        }
+        return acc;
+      };
+      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile);
       if (lane == 0) Desc<uint32_t>::publish(desc, tile, kInc, prefix + agg);
     }
     if (lane == 0) {
@@ -138,7 +173,7 @@ __global__ __launch_bounds__(256) void select_kernel(uintptr_t in_base, uintptr_
   const int s0 = (int)((g + out_ph) % EO);             // slot of the first selected element
   uint32_t before = 0u, count = 0u;
 #pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) {
+  for (int w = 0; w < WPB; ++w) {
     const uint32_t c = s_wave[w];
     before += (w < wave) ? c : 0u;
     count += c;
@@ -155,60 +190,68 @@ __global__ __launch_bounds__(256) void select_kernel(uintptr_t in_base, uintptr_
   const int64_t gv0 = (g + out_ph) / EO;               // first output vector of the run
   const int end = s0 + (int)count;
   const int nvec = (end + EO - 1) / EO;
-  for (int w = (int)threadIdx.x; w < nvec; w += kBlock) {
+  for (int w = (int)threadIdx.x; w < nvec; w += kThreads) {
     const int slot0 = w * EO;
     const uintptr_t dst = out_base + (uintptr_t)(gv0 + w) * 16;
     if (slot0 >= s0 && slot0 + EO <= end) {
-      *(uint4*)dst = *(const uint4*)&s_stage[slot0];
+      __builtin_nontemporal_store(*(const u32x4*)&s_stage[slot0], gptr<u32x4>(dst));
     } else {
 #pragma unroll
       for (int k = 0; k < EO; ++k) {
         const int slot = slot0 + k;
-        if (slot >= s0 && slot < end) *(T*)(dst + (uintptr_t)k * EB) = s_stage[slot];
+        if (slot >= s0 && slot < end) *gptr<T>(dst + (uintptr_t)k * EB) = s_stage[slot];
       }
     }
   }
 }
 
-static int64_t sel_tiles_for(int64_t n, int e) {
+// Tiles of tv vectors covering window elements [ph, n + ph) (ph < e).
+static int64_t sel_tiles_for(int64_t n, int e, int64_t tv) {
   if (n <= 0) return 0;
   const int64_t v_last = (n - 1 + (e - 1)) / e;
-  return v_last / kSelTileVecs + 1;
+  return v_last / tv + 1;
 }
 
-// Sized for 8-byte elements (two per vector, the most tiles) so one scratch
-// size serves both element widths.
+// Sized for 8-byte elements (two per vector, the most tiles) and the smallest
+// tile, so one scratch size serves both element widths and every launch shape.
 size_t select_tiles(int64_t n, size_t elem_bytes) {
   (void)elem_bytes;
-  return (size_t)sel_tiles_for(n, 2);
+  return (size_t)sel_tiles_for(n, 2, kSelMinTileVecs);
 }
 
 __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
 
-template <int EB>
-static hipError_t launch_sel_t(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                               int64_t n, void* scratch, hipStream_t stream) {
+// One launch shape: WPB waves per workgroup, K vectors per lane per tile.
+template <int EB, int WPB, int K>
+static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                                 int64_t n, void* scratch, hipStream_t stream) {
   constexpr int E = 16 / EB;
+  constexpr int64_t TV = (int64_t)kWave * WPB * K;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
   const int64_t ph = (int64_t)((ia % 16) / EB);
   const int64_t out_ph = (int64_t)((oa % 16) / EB);
   const uintptr_t fbase = fa - (uintptr_t)ph;          // flag byte of window element 0
   const bool fvec = (fbase % E) == 0;
-  const int64_t ntiles = sel_tiles_for(n, E);
-  uint32_t* counter = (uint32_t*)scratch;
-  uint64_t* desc = (uint64_t*)((char*)scratch + kScratchHeader);
-  hipError_t err = launch_fill_zero(scratch, kScratchHeader + (size_t)ntiles * 8, stream);
+  const int64_t ntiles = sel_tiles_for(n, E, TV);
+  uint64_t* desc = (uint64_t*)scratch;
+  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * 8, stream);
   if (err != hipSuccess) return err;
-  const dim3 grid((unsigned)ntiles), block(kBlock);
+  const dim3 grid((unsigned)ntiles), block(64 * WPB);
   const uintptr_t ibase = ia - (uintptr_t)ph * EB, obase = oa - (uintptr_t)out_ph * EB;
   if (fvec) {
-    select_kernel<EB, E, true, kSelK><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, counter, desc);
+    select_kernel<EB, E, true, WPB, K><<<grid, block, 0, stream>>>(
+        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
   } else {
-    select_kernel<EB, E, false, kSelK><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, counter, desc);
+    select_kernel<EB, E, false, WPB, K><<<grid, block, 0, stream>>>(
+        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
   }
   return hipGetLastError();
+}
+
+template <int EB>
+static hipError_t launch_sel_t(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                               int64_t n, void* scratch, hipStream_t stream) {
+  return launch_sel_cfg<EB, 4, 8>(in, flags, out, num_out, n, scratch, stream);
 }
 
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,

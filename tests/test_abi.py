@@ -84,7 +84,7 @@ def test_scan_device_validation():
     i32 = D["i32"]
     add = OP["add"]
     need = L.scan_device_scratch_bytes(1000, i32)
-    assert need >= 256 and need % 16 == 0
+    assert need >= 16 and need % 16 == 0
     assert L.scan_device_scratch_bytes(-1, i32) == 0
     assert L.scan_device(A, B, 1000, D["bf16"], add, S, need, None) == ENOTSUP
     assert L.scan_device(A, B, 1000, i32, 7, S, need, None) == ENOTSUP
@@ -102,7 +102,8 @@ def test_scan_device_validation():
         small = L.scan_device_scratch_bytes(1 << 20, D[name])
         big = L.scan_device_scratch_bytes(1 << 28, D[name])
         assert big > small > 0
-        assert big < (1 << 28) // 64                 # a small fraction of the data
+        eb = 8 if name in ("i64", "u64", "f64") else 4
+        assert big < (1 << 28) * eb // 100           # under 1% of the input bytes
 
 
 def test_select_validation():
@@ -118,7 +119,7 @@ def test_select_validation():
     assert L.select_compact(A, S + 0x10000, B, N, 1000, 4, S, need - 16, None) == ESCRATCH
     assert L.select_compact(A, S + 0x10000, A + 100, N, 1000, 4, S, need, None) == EALIAS
     assert L.select_compact(A, S + 0x10000, B, B + 40, 1000, 4, S, need, None) == EALIAS
-    assert L.select_compact(A, S + 16, B, N, 1000, 4, S, need, None) == EALIAS   # flags in scratch
+    assert L.select_compact(A, S + 8, B, N, 1000, 4, S, need, None) == EALIAS    # flags in scratch
 
 
 def test_binding_maps_status_to_exceptions():

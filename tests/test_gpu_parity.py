@@ -90,10 +90,15 @@ def _gpu():
 # row-wise scans
 # ---------------------------------------------------------------------------
 
-ROW_SHAPES = [(1, 1), (1, 2), (3, 3), (3, 5), (1, 63), (3, 64), (5, 65), (3, 255), (3, 256),
-              (3, 257), (2, 511), (3, 513), (2, 1023), (2, 1024), (3, 1025), (2, 2047), (3, 2049),
-              (2, 4351), (2, 4352), (3, 4353), (2, 8703), (2, 8704), (3, 8705), (2, 20000),
-              (7, 333), (33, 100)]
+# covers every launch-shape boundary of the row kernel for 4- and 2-byte
+# elements (rows touching 64, 256, 1024 and 1280 16-byte vectors) and rows
+# long enough to take several chunks
+ROW_SHAPES = [(1, 1), (1, 2), (3, 3), (3, 5), (1, 63), (3, 64), (5, 65), (2, 250), (3, 251),
+              (3, 255), (3, 256), (3, 257), (2, 498), (3, 499), (2, 511), (3, 513), (2, 1018),
+              (3, 1019), (2, 1023), (2, 1024), (3, 1025), (2, 2034), (3, 2035), (2, 2047),
+              (3, 2049), (2, 4090), (3, 4091), (2, 4351), (2, 4352), (3, 4353), (2, 5114),
+              (3, 5115), (2, 8178), (3, 8179), (2, 8703), (2, 8704), (3, 8705), (2, 10226),
+              (3, 10227), (2, 20000), (3, 50001), (7, 333), (33, 100)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
@@ -385,3 +390,55 @@ def test_select_empty():
     num = torch.full((1,), 123, dtype=torch.int32, device="cuda")
     sc.select_compact(x, f, num_out=num)
     assert int(num.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# look-back recovery: a test-only build whose look-back never waits, so every
+# predecessor descriptor that is not yet published is recomputed from the
+# input by the waiting tile.  Results must be identical.
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return t.data_ptr()
+
+
+def test_lookback_recovery_build_device_scan():
+    from stream_compaction_amd import build as b
+    L = sc.load(b.FALLBACK_LIB_PATH)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i, (dt, op, n) in enumerate([("i32", "add", 3_000_001), ("f32", "min", 1_000_003),
+                                     ("i64", "max", 700_001), ("u64", "add", 500_000),
+                                     ("f64", "add", 400_003), ("u32", "max", 2_000_000)]):
+        x = rand_input(dt, n, 5000 + i)
+        xd = to_dev(x, dt)
+        yd = torch.empty_like(xd)
+        code = sc.DTYPE_CODES[dt]
+        need = L.scan_device_scratch_bytes(n, code)
+        scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+        sc.check(L.scan_device(_ptr(xd), _ptr(yd), n, code, sc.OP_CODES[op], _ptr(scratch), need,
+                               stream))
+        torch.cuda.synchronize()
+        compare_scan(from_dev(yd, dt), x, dt, op, True, f"recovery build scan_device {dt} {op}")
+
+
+def test_lookback_recovery_build_select():
+    from stream_compaction_amd import build as b
+    L = sc.load(b.FALLBACK_LIB_PATH)
+    stream = torch.cuda.current_stream().cuda_stream
+    for eb, n, p in ((4, 2_000_003, 0.5), (8, 1_000_001, 0.3)):
+        rng = np.random.default_rng(eb)
+        x = rng.integers(0, 1 << 62, size=n, dtype=np.int64)
+        x = x.astype(np.uint32) if eb == 4 else x.astype(np.uint64)
+        flags = workloads.bernoulli_flags(n, p, 60 + eb)
+        xd = torch.from_numpy(x.view(np.int32 if eb == 4 else np.int64).copy()).cuda()
+        fd = torch.from_numpy(flags).cuda()
+        out = torch.zeros_like(xd)
+        num = torch.zeros(1, dtype=torch.int32, device="cuda")
+        need = L.select_compact_scratch_bytes(n)
+        scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+        sc.check(L.select_compact(_ptr(xd), _ptr(fd), _ptr(out), _ptr(num), n, eb, _ptr(scratch),
+                                  need, stream))
+        k = int(num.item())
+        ora, ko = oracle.select(x, flags)
+        assert k == ko
+        check_exact(out.cpu().numpy().view(x.dtype)[:k], ora[:k], f"recovery build select eb={eb}")
