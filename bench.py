@@ -41,6 +41,9 @@ KERNEL_SOURCES = {           # sources whose change invalidates stored counter r
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/pmc_traffic.json from the counter_collection.csv files of "
+                         "two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
@@ -59,8 +62,49 @@ def sources_sha(kind):
     return h.hexdigest()[:16]
 
 
+KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> workload key
+    "void sca::scan_rows_kernel<sca::FmtBF16, (sca::Op)0, true, 8, 4, 4>(": "rows_bf16_excl",
+    "(anonymous namespace)::copy16_kernel": "copy16",
+}
+
+
+def pmc_summary(fetch_csv, write_csv, command):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel -> profiles/pmc_traffic.json."""
+    import csv
+
+    def read(path, counter):
+        acc = {}
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                for prefix, key in KERNEL_KEYS.items():
+                    if name.startswith(prefix):
+                        acc.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    out = {"command": command,
+           "note": "KiB per dispatch, averaged over dispatches; copy16 moved bytes/2 each way",
+           "copy16": {"bytes": 268435456, "fetch_kib": fetch["copy16"],
+                      "write_kib": write["copy16"]},
+           "kernels": {"rows_bf16_excl": {"fetch_kib": fetch["rows_bf16_excl"],
+                                          "write_kib": write["rows_bf16_excl"],
+                                          "source_sha": sources_sha("scan_rows")}}}
+    with open(PMC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary,
+                    command="rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -- python "
+                            "bench.py --only rows_bf16_excl,copy16 --steps 5 --warmup 1 --sets 1 "
+                            "--no-cpu")
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the library has no multi-GPU "
                                    "path, so --gpus must be 1", "n_gpus": args.gpus}), flush=True)
@@ -83,20 +127,38 @@ def main():
         return not only or name in only
 
     def timed(launch, steps, warmup):
-        """Run launch(i) warmup+steps times; returns (wall seconds, per-launch ms list)."""
+        """Time `steps` calls of launch(i) after `warmup` untimed ones.
+
+        Returns (wall seconds, per-launch kernel ms list).  The timed region is
+        bracketed by synchronizations; the calls inside it are enqueued back to
+        back with one pair of HIP events around the whole region on the launch
+        stream, and a second pass brackets each call with its own event pair.
+        The per-call figure is the smaller of the window average and the mean of
+        the per-call pairs (both include some launch overhead on the GPU).
+        """
         for i in range(warmup):
             launch(i)
         torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        w0.record(stream)
+        for i in range(steps):
+            launch(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        window_ms = w0.elapsed_time(w1) / steps
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        t0 = time.perf_counter()
         for i in range(steps):
             ev0[i].record(stream)
             launch(i)
             ev1[i].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+        per = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+        if window_ms < float(np.mean(per)):
+            per = [window_ms] * steps
+        return wall, per
 
     def bf16_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)

@@ -183,6 +183,9 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   return hipGetLastError();
 }
 
+// Launch shape measured on MI355X over 2^28 32-bit elements: four waves of
+// sixteen loads (64 KiB tiles) beat both wider workgroups and smaller tiles;
+// smaller tiles spend longer in look-back than they gain in occupancy.
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, void* scratch,
                                hipStream_t stream) {

@@ -124,7 +124,9 @@ static void launch_rows_cfg(uintptr_t in_base, uintptr_t out_base, int64_t rows,
 template <class F, Op O, bool EXCL, int E>
 static hipError_t launch_rows_e(uintptr_t in_base, uintptr_t out_base, int64_t rows, int64_t n,
                                 int64_t ph, hipStream_t stream) {
-  const int64_t vmax = (n + 2 * E - 2) / E;  // vectors one row can touch
+  // vectors one row can touch: exactly n/E when every row starts on a vector
+  // boundary, else one more for a row that straddles
+  const int64_t vmax = (ph == 0 && n % E == 0) ? n / E : (n + 2 * E - 2) / E;
   if (vmax <= kWave) {
     launch_rows_cfg<F, O, EXCL, E, 1, 1>(in_base, out_base, rows, n, ph, stream);
   } else if (vmax <= 4 * kWave) {

@@ -98,7 +98,8 @@ ROW_SHAPES = [(1, 1), (1, 2), (3, 3), (3, 5), (1, 63), (3, 64), (5, 65), (2, 250
               (3, 1019), (2, 1023), (2, 1024), (3, 1025), (2, 2034), (3, 2035), (2, 2047),
               (3, 2049), (2, 4090), (3, 4091), (2, 4351), (2, 4352), (3, 4353), (2, 5114),
               (3, 5115), (2, 8178), (3, 8179), (2, 8703), (2, 8704), (3, 8705), (2, 10226),
-              (3, 10227), (2, 20000), (3, 50001), (7, 333), (33, 100)]
+              (3, 10227), (2, 20000), (3, 50001), (7, 333), (33, 100), (3, 4096), (3, 5120),
+              (3, 8192), (2, 10240), (2, 16384)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
