@@ -414,13 +414,33 @@ template <class W> struct Desc<W, 8> {
 // changes, so this is exactly what that tile would publish).  The walk then
 // needs nothing from workgroups that have not started, so it ends whatever
 // order the hardware runs workgroups in; in the usual case no descriptor is
-// that late and no tile is reduced twice.
-template <Op O, class W, class ReduceTile>
+// that late and no tile is reduced twice.  idle() runs between polls (the
+// caller publishes its own aggregate there as soon as it is known).
+// Pause between descriptor polls: s_sleep 127 (about 8k cycles, ~3.4 us).
+// Polling is not free on MI355X: every poll is a device-scope read that goes
+// past the XCD's L2, and with a thousand tiles waiting at once short pauses
+// measurably slowed the data traffic (2^28 i32 scan: 517 us at s_sleep 1,
+// 443 us at 100, 436 us at 127).
+constexpr int kPollSleep = 127;
+
+template <Op O, class W, class ReduceTile, class Idle>
 __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint64_t timeout,
-                                       ReduceTile&& reduce_tile) {
+                                       ReduceTile&& reduce_tile, Idle&& idle) {
   const int lane = lane_id();
   const W id = identity<O, W>();
   W prefix = id;
+  {
+    // Wait on the nearest predecessor alone first: it started last, so it is
+    // usually the last to publish, and one descriptor per poll keeps the
+    // polling traffic small while many tiles wait at once.
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    W v;
+    while (Desc<W>::read(desc, tile - 1, v) == kNone &&
+           __builtin_amdgcn_s_memrealtime() - t0 <= timeout) {
+      idle();
+      __builtin_amdgcn_s_sleep(kPollSleep);
+    }
+  }
   for (int64_t base = tile - 1;; base -= kWave) {
     const int64_t t = base - (kWave - 1) + lane;
     W v = id;
@@ -446,7 +466,8 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
         }
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      idle();
+      __builtin_amdgcn_s_sleep(kPollSleep);
     }
     const uint64_t inc = __ballot(st == kInc);
     const int stop = inc ? 63 - __builtin_clzll(inc) : 0;

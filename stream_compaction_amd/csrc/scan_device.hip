@@ -3,47 +3,58 @@
 // qd.algorithms.exclusive_scan_{add,min,max} for the contract, "Related" for
 // decoupled look-back as the alternative to a phase-per-launch staircase).
 //
-// Workgroup b owns tile b (WPB waves, K 16-byte vectors per lane).  It loads
-// its tile (load j of lane l in wave w is vector (w*K + j)*64 + l of the
-// tile, so every load instruction covers 1 KiB of contiguous memory) and:
-//   1. scans every vector lane-serially, then the 64 lane totals with a DPP
-//      wave scan, keeping per vector the combine of everything before it in
-//      the wave;
-//   2. publishes the wave totals through LDS; wave 0 forms the tile
-//      aggregate, publishes it, looks back over predecessor descriptors to
-//      get the tile's exclusive prefix, and publishes its inclusive prefix;
-//   3. after one more barrier every lane combines tile prefix, earlier waves,
-//      earlier vectors and earlier elements of its vector, and stores.
+// Workgroup b owns tile b.  It has WD data waves and one look-back wave.
+//  - Each data wave loads its run of 64*K 16-byte vectors (load j of lane l
+//    is vector j*64 + l of the run, so every load instruction covers 1 KiB),
+//    scans every vector lane-serially and the 64 lane totals with a DPP wave
+//    scan, and posts its wave total to LDS.
+//  - The look-back wave starts walking back over the predecessors'
+//    descriptors as soon as the workgroup starts, while the data is still in
+//    flight: the walk needs nothing from this tile.  Between polls it
+//    publishes the tile's aggregate once all wave totals are posted; when the
+//    walk ends it publishes the tile's inclusive prefix and hands the
+//    exclusive prefix to the data waves through LDS.
+//  - The data waves then combine tile prefix, earlier waves, earlier vectors
+//    and earlier elements of the vector, and store.
 // The input is read once and the output written once.  Tile ids are the
 // workgroup ids: no atomic counter (a device-wide atomic on one address
 // serializes at about 11 ns per tile on MI355X); the look-back's bounded wait
 // (device.hpp) keeps this correct and deadlock-free under any workgroup order.
+// The look-back wave learns that the wave totals are posted from an LDS
+// counter (no barrier), so it never holds up the data waves' loads and scans;
+// one barrier then hands the prefix back, with the data waves asleep in it.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace sca {
 
 // Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
-constexpr int64_t kDevMinTileVecs = 1024;
+constexpr int64_t kDevMinTileVecs = 512;
 
-template <class F, Op O, int E, int WPB, int K>
-__global__ __launch_bounds__(64 * WPB) void scan_device_kernel(uintptr_t in_base, uintptr_t out_base,
-                                                              int64_t n, int64_t ph, int64_t ntiles,
-                                                              uint64_t* desc) {
+__device__ __forceinline__ uint32_t lds_acquire(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <class F, Op O, int E, int WD, int K>
+__global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
+    uintptr_t in_base, uintptr_t out_base, int64_t n, int64_t ph, int64_t ntiles, uint64_t* desc) {
   using S = typename F::S;
   using W = typename F::W;
   using IO = VecIO<S, E>;
   constexpr int64_t VB = (int64_t)E * sizeof(S);       // bytes per vector
   constexpr int64_t kWaveVecs = (int64_t)kWave * K;
-  constexpr int64_t kTileVecs = kWaveVecs * WPB;
+  constexpr int64_t kTileVecs = kWaveVecs * WD;
   static_assert(kTileVecs >= kDevMinTileVecs, "scratch is sized for the smallest tile");
-  __shared__ W s_wave[WPB];
+  __shared__ W s_wave[WD];
   __shared__ W s_prefix;
+  __shared__ uint32_t s_posted;   // data waves whose totals are in s_wave
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const W id = identity<O, W>();
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  if (threadIdx.x == 0) s_posted = 0u;
+  __syncthreads();
 
   // A wave's K loads of the run of 64*K vectors starting at `first` (zero bits past v_last).
   auto load = [&](int64_t first, typename IO::Raw (&raw)[K]) {
@@ -62,40 +73,62 @@ __global__ __launch_bounds__(64 * WPB) void scan_device_kernel(uintptr_t in_base
     }
   };
 
-  const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
-  typename IO::Raw raw[K];
-  load(wb, raw);
-
-  // 1. within the wave
-  W x[K][E];
-  W pre[K];
-  W carry = id;
+  if (wave < WD) {
+    // ---- data wave ----
+    const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
+    typename IO::Raw raw[K];
+    load(wb, raw);
+    W x[K][E];
+    W pre[K];
+    W carry = id;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    unpack(wb + j * kWave, raw[j], x[j]);
+    for (int j = 0; j < K; ++j) {
+      unpack(wb + j * kWave, raw[j], x[j]);
 #pragma unroll
-    for (int k = 1; k < E; ++k) x[j][k] = combine<O>(x[j][k - 1], x[j][k]);
-    const W incl = wave_scan_incl<O>(x[j][E - 1]);
-    pre[j] = combine<O>(carry, wave_shift_excl<O>(incl));
-    carry = combine<O>(carry, readlane(incl, kWave - 1));
-  }
-  if (lane == 0) s_wave[wave] = carry;
-  __syncthreads();
-
-  // 2. across tiles
-  if (wave == 0) {
-    W agg = s_wave[0];
+      for (int k = 1; k < E; ++k) x[j][k] = combine<O>(x[j][k - 1], x[j][k]);
+      const W incl = wave_scan_incl<O>(x[j][E - 1]);
+      pre[j] = combine<O>(carry, wave_shift_excl<O>(incl));
+      carry = combine<O>(carry, readlane(incl, kWave - 1));
+    }
+    if (lane == 0) {
+      s_wave[wave] = carry;
+      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();  // sleeps in hardware until the look-back wave has the prefix
+    W wp = s_prefix;
+    for (int w = 0; w < wave; ++w) wp = combine<O>(wp, s_wave[w]);
 #pragma unroll
-    for (int w = 1; w < WPB; ++w) agg = combine<O>(agg, s_wave[w]);
+    for (int j = 0; j < K; ++j) {
+      const W q = combine<O>(wp, pre[j]);
+      W y[E];
+      y[0] = q;
+#pragma unroll
+      for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
+      const int64_t v = wb + j * kWave + lane;
+      if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+    }
+  } else {
+    // ---- look-back wave ----
+    auto posted = [&]() { return lds_acquire(&s_posted) == (uint32_t)WD; };
+    auto tile_agg = [&]() {
+      W a = s_wave[0];
+#pragma unroll
+      for (int w = 1; w < WD; ++w) a = combine<O>(a, s_wave[w]);
+      return a;
+    };
     W prefix = id;
-    if (tile == 0) {
-      if (lane == 0) Desc<W>::publish(desc, tile, kInc, agg);
-    } else {
-      if (lane == 0) Desc<W>::publish(desc, tile, kAgg, agg);
+    if (tile > 0) {
+      bool agg_published = false;
+      auto idle = [&]() {
+        if (!agg_published && posted()) {
+          if (lane == 0) Desc<W>::publish(desc, tile, kAgg, tile_agg());
+          agg_published = true;
+        }
+      };
       // fallback for a late predecessor: reduce its input in element order
       auto reduce_tile = [&](int64_t t) -> W {
         W acc = id;
-        for (int c = 0; c < WPB; ++c) {
+        for (int c = 0; c < WD; ++c) {
           typename IO::Raw r[K];
           const int64_t first = t * kTileVecs + c * kWaveVecs;
           load(first, r);
@@ -110,25 +143,14 @@ __global__ __launch_bounds__(64 * WPB) void scan_device_kernel(uintptr_t in_base
         }
         return acc;
       };
-      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile);
-      if (lane == 0) Desc<W>::publish(desc, tile, kInc, combine<O>(prefix, agg));
+      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile, idle);
     }
-    if (lane == 0) s_prefix = prefix;
-  }
-  __syncthreads();
-
-  // 3. outputs
-  W wp = s_prefix;
-  for (int w = 0; w < wave; ++w) wp = combine<O>(wp, s_wave[w]);
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const W q = combine<O>(wp, pre[j]);
-    W y[E];
-    y[0] = q;
-#pragma unroll
-    for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
-    const int64_t v = wb + j * kWave + lane;
-    if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+    while (!posted()) __builtin_amdgcn_s_sleep(1);
+    if (lane == 0) {
+      Desc<W>::publish(desc, tile, kInc, combine<O>(prefix, tile_agg()));
+      s_prefix = prefix;
+    }
+    __syncthreads();
   }
 }
 
@@ -157,13 +179,14 @@ size_t scan_device_tiles(int64_t n, Fmt fmt) {
   return (size_t)tiles_for(n, 1, kDevMinTileVecs);
 }
 
-// One launch shape: WPB waves per workgroup, K vectors per lane per tile.
-template <class F, Op O, int WPB, int K>
+// One launch shape: WD data waves (plus the look-back wave), K vectors per
+// lane per tile.
+template <class F, Op O, int WD, int K>
 static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
                                  hipStream_t stream) {
   using S = typename F::S;
   constexpr int EV = 16 / (int)sizeof(S);
-  constexpr int64_t TV = (int64_t)kWave * WPB * K;
+  constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
   uint64_t* desc = (uint64_t*)scratch;
   const bool vec = (ia % 16) == (oa % 16);
@@ -173,23 +196,24 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * Desc<typename F::W>::kWords * 8,
                                     stream);
   if (err != hipSuccess) return err;
-  const dim3 grid((unsigned)ntiles), block(64 * WPB);
+  const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   if (vec) {
-    scan_device_kernel<F, O, EV, WPB, K><<<grid, block, 0, stream>>>(
+    scan_device_kernel<F, O, EV, WD, K><<<grid, block, 0, stream>>>(
         ia - ph * sizeof(S), oa - ph * sizeof(S), n, ph, ntiles, desc);
   } else {
-    scan_device_kernel<F, O, 1, WPB, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles, desc);
+    scan_device_kernel<F, O, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles, desc);
   }
   return hipGetLastError();
 }
 
-// Launch shape measured on MI355X over 2^28 32-bit elements: four waves of
-// sixteen loads (64 KiB tiles) beat both wider workgroups and smaller tiles;
-// smaller tiles spend longer in look-back than they gain in occupancy.
+// Launch shape measured on MI355X over 2^28 32-bit elements (us per scan):
+// 7 data waves x 16 loads (112 KiB tiles) 411, 3 x 20: 416, 3 x 16: 436,
+// 4 x 16: 525, 3 x 8: 527.  Few, large tiles win: each tile's look-back costs
+// microseconds of latency, and registers (not LDS) bound the tile size.
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, void* scratch,
                                hipStream_t stream) {
-  return launch_dev_cfg<F, O, 4, 16>(in, out, n, scratch, stream);
+  return launch_dev_cfg<F, O, 7, 16>(in, out, n, scratch, stream);
 }
 
 template <class F>

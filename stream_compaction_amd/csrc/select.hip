@@ -6,13 +6,15 @@
 // into an n-entry index buffer, scatter, one-thread count; section "Under the
 // hood").  Here one kernel does all of it in a single pass, with the scan of
 // the flag counts done by the same DPP wave scan and decoupled look-back as
-// the device-wide scan, and no index buffer:
-//   1. each lane loads 16-byte payload vectors (load j of lane l is vector
-//      j*64 + l of its wave's segment) and the matching flag bytes, and forms
-//      a bit mask of its selected elements;
-//   2. lane counts are scanned across the wave (DPP), wave totals across the
-//      workgroup (LDS), and the tile count across tiles (look-back), giving
-//      the tile's output offset G; the tile with the last id writes num_out;
+// the device-wide scan, and no index buffer.  Workgroup b owns tile b; it has
+// WD data waves and one look-back wave:
+//   1. each data wave loads 16-byte payload vectors (load j of lane l is
+//      vector j*64 + l of its run) and the matching flag bytes, and forms a
+//      bit mask of its selected elements;
+//   2. lane counts are scanned across the wave (DPP) and posted to LDS; the
+//      look-back wave, walking back over the predecessors' descriptors from
+//      the start, publishes the tile's count once posted and then the tile's
+//      output offset G; the tile with the last id writes num_out;
 //   3. selected elements are packed into LDS at their rank, shifted so LDS
 //      vectors line up with 16-byte vectors of `out`, and the workgroup
 //      stores the packed run [G, G + count) with 16-byte stores (element
@@ -25,32 +27,35 @@
 namespace sca {
 
 // Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
-constexpr int64_t kSelMinTileVecs = 1024;
+constexpr int64_t kSelMinTileVecs = 512;
 
 template <int EB> struct Bits;
 template <> struct Bits<4> { using T = uint32_t; };
 template <> struct Bits<8> { using T = uint64_t; };
 
-template <int EB, int E, bool FVEC, int WPB, int K>
-__global__ __launch_bounds__(64 * WPB) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
+template <int EB, int E, bool FVEC, int WD, int K>
+__global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
                                                          uintptr_t out_base, int64_t n, int64_t ph,
                                                          int64_t out_ph, int64_t ntiles,
                                                          int32_t* num_out, uint64_t* desc) {
   using T = typename Bits<EB>::T;
   constexpr int EO = 16 / EB;                     // elements per 16-byte output vector
-  constexpr int kThreads = kWave * WPB;
+  constexpr int kThreads = kWave * (WD + 1);
   constexpr int64_t kWaveVecs = (int64_t)kWave * K;
-  constexpr int64_t kTileVecs = kWaveVecs * WPB;
+  constexpr int64_t kTileVecs = kWaveVecs * WD;
   static_assert(kTileVecs >= kSelMinTileVecs, "scratch is sized for the smallest tile");
   constexpr int kTileElems = (int)kTileVecs * E;
   constexpr int64_t VB = (int64_t)E * EB;
   __shared__ __attribute__((aligned(16))) T s_stage[kTileElems + EO];
-  __shared__ uint32_t s_wave[WPB];
+  __shared__ uint32_t s_wave[WD];
   __shared__ uint32_t s_prefix;
+  __shared__ uint32_t s_posted;   // data waves whose counts are in s_wave
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  if (threadIdx.x == 0) s_posted = 0u;
+  __syncthreads();
 
   // Flag bytes of the run of 64*K vectors starting at `first` (E bytes per
   // vector, packed low byte first; zero past v_last).
@@ -89,65 +94,82 @@ __global__ __launch_bounds__(64 * WPB) void select_kernel(uintptr_t in_base, uin
     return m;
   };
 
-  // 1. payload and selection masks: every load is issued unconditionally through
-  //    buffer resources that end at the wave's last valid vector (past it: zero
-  //    bits, i.e. unselected); only the two end vectors of the array need masking
+  // 1. payload and selection masks (data waves): every load is issued
+  //    unconditionally through buffer resources that end at the wave's last
+  //    valid vector (past it: zero bits, i.e. unselected); only the two end
+  //    vectors of the array need masking
   const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
   T x[K][E];
-  uint32_t f[K];
-  {
-    const int64_t left = v_last + 1 - wb;
-    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
-    const Buf pbuf(in_base + wb * VB, nv * VB);
+  uint32_t m[K];
+  uint32_t pre[K];
+  if (wave < WD) {
+    uint32_t f[K];
+    {
+      const int64_t left = v_last + 1 - wb;
+      const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+      const Buf pbuf(in_base + wb * VB, nv * VB);
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const uint32_t u = (uint32_t)(j * kWave + lane);
-      if constexpr (E == 1) {
-        if constexpr (EB == 4) {
-          x[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(pbuf.r, u * 4, 0, kNT);
+      for (int j = 0; j < K; ++j) {
+        const uint32_t u = (uint32_t)(j * kWave + lane);
+        if constexpr (E == 1) {
+          if constexpr (EB == 4) {
+            x[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(pbuf.r, u * 4, 0, kNT);
+          } else {
+            x[j][0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(pbuf.r, u * 8, 0, kNT));
+          }
         } else {
-          x[j][0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(pbuf.r, u * 8, 0, kNT));
-        }
-      } else {
-        const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, u * 16, 0, kNT));
-        if constexpr (EB == 4) {
-          x[j][0] = r.x; x[j][1] = r.y; x[j][2] = r.z; x[j][3] = r.w;
-        } else {
-          x[j][0] = ((uint64_t)r.y << 32) | r.x;
-          x[j][1] = ((uint64_t)r.w << 32) | r.z;
+          const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, u * 16, 0, kNT));
+          if constexpr (EB == 4) {
+            x[j][0] = r.x; x[j][1] = r.y; x[j][2] = r.z; x[j][3] = r.w;
+          } else {
+            x[j][0] = ((uint64_t)r.y << 32) | r.x;
+            x[j][1] = ((uint64_t)r.w << 32) | r.z;
+          }
         }
       }
     }
-  }
-  load_flags(wb, f);
-  uint32_t m[K];
+    load_flags(wb, f);
 #pragma unroll
-  for (int j = 0; j < K; ++j) m[j] = select_mask(wb + j * kWave, f[j]);
+    for (int j = 0; j < K; ++j) m[j] = select_mask(wb + j * kWave, f[j]);
 
-  // 2. ranks: within the wave, across waves, across tiles
-  uint32_t pre[K];
-  uint32_t carry = 0u;
+    // 2. ranks within the wave; the wave's count goes to LDS
+    uint32_t carry = 0u;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const uint32_t incl = wave_scan_incl<Op::Add>((uint32_t)__builtin_popcount(m[j]));
-    pre[j] = carry + wave_shift_excl<Op::Add>(incl);
-    carry += readlane(incl, kWave - 1);
-  }
-  if (lane == 0) s_wave[wave] = carry;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t agg = 0u;
+    for (int j = 0; j < K; ++j) {
+      const uint32_t incl = wave_scan_incl<Op::Add>((uint32_t)__builtin_popcount(m[j]));
+      pre[j] = carry + wave_shift_excl<Op::Add>(incl);
+      carry += readlane(incl, kWave - 1);
+    }
+    if (lane == 0) {
+      s_wave[wave] = carry;
+      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  } else {
+    // 2'. the look-back wave: walks back from the start, publishes the tile's
+    //     count as soon as all waves posted it, and the tile's output offset
+    auto posted = [&]() {
+      return __hip_atomic_load(&s_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+             (uint32_t)WD;
+    };
+    auto tile_count = [&]() {
+      uint32_t a = 0u;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) agg += s_wave[w];
+      for (int w = 0; w < WD; ++w) a += s_wave[w];
+      return a;
+    };
     uint32_t prefix = 0u;
-    if (tile == 0) {
-      if (lane == 0) Desc<uint32_t>::publish(desc, tile, kInc, agg);
-    } else {
-      if (lane == 0) Desc<uint32_t>::publish(desc, tile, kAgg, agg);
+    if (tile > 0) {
+      bool agg_published = false;
+      auto idle = [&]() {
+        if (!agg_published && posted()) {
+          if (lane == 0) Desc<uint32_t>::publish(desc, tile, kAgg, tile_count());
+          agg_published = true;
+        }
+      };
       // fallback for a late predecessor: count its selected flags
       auto reduce_tile = [&](int64_t t) -> uint32_t {
         uint32_t acc = 0u;
-        for (int c = 0; c < WPB; ++c) {
+        for (int c = 0; c < WD; ++c) {
           const int64_t first = t * kTileVecs + c * kWaveVecs;
           uint32_t g[K];
           load_flags(first, g);
@@ -158,32 +180,36 @@ __global__ __launch_bounds__(64 * WPB) void select_kernel(uintptr_t in_base, uin
         }
         return acc;
       };
-      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile);
-      if (lane == 0) Desc<uint32_t>::publish(desc, tile, kInc, prefix + agg);
+      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile, idle);
     }
+    while (!posted()) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
+      const uint32_t agg = tile_count();
+      Desc<uint32_t>::publish(desc, tile, kInc, prefix + agg);
       s_prefix = prefix;
       if (tile == ntiles - 1) *num_out = (int32_t)(prefix + agg);
     }
   }
   __syncthreads();
 
-  // 3. pack into LDS, then store the run with 16-byte vectors
+  // 3. pack the selected elements into LDS, then store the run with 16-byte vectors
   const int64_t g = (int64_t)s_prefix;                 // output offset of this tile
-  const int s0 = (int)((g + out_ph) % EO);             // slot of the first selected element
   uint32_t before = 0u, count = 0u;
 #pragma unroll
-  for (int w = 0; w < WPB; ++w) {
+  for (int w = 0; w < WD; ++w) {
     const uint32_t c = s_wave[w];
     before += (w < wave) ? c : 0u;
     count += c;
   }
+  const int s0 = (int)((g + out_ph) % EO);             // slot of the first selected element
+  if (wave < WD) {
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    uint32_t r = (uint32_t)s0 + before + pre[j];
+    for (int j = 0; j < K; ++j) {
+      uint32_t r = (uint32_t)s0 + before + pre[j];
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      if ((m[j] >> k) & 1u) s_stage[r++] = x[j][k];
+      for (int k = 0; k < E; ++k) {
+        if ((m[j] >> k) & 1u) s_stage[r++] = x[j][k];
+      }
     }
   }
   __syncthreads();
@@ -221,12 +247,13 @@ size_t select_tiles(int64_t n, size_t elem_bytes) {
 
 __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
 
-// One launch shape: WPB waves per workgroup, K vectors per lane per tile.
-template <int EB, int WPB, int K>
+// One launch shape: WD data waves (plus the look-back wave), K vectors per
+// lane per tile.
+template <int EB, int WD, int K>
 static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                                  int64_t n, void* scratch, hipStream_t stream) {
   constexpr int E = 16 / EB;
-  constexpr int64_t TV = (int64_t)kWave * WPB * K;
+  constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
   const int64_t ph = (int64_t)((ia % 16) / EB);
   const int64_t out_ph = (int64_t)((oa % 16) / EB);
@@ -236,25 +263,27 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
   uint64_t* desc = (uint64_t*)scratch;
   hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * 8, stream);
   if (err != hipSuccess) return err;
-  const dim3 grid((unsigned)ntiles), block(64 * WPB);
+  const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ibase = ia - (uintptr_t)ph * EB, obase = oa - (uintptr_t)out_ph * EB;
   if (fvec) {
-    select_kernel<EB, E, true, WPB, K><<<grid, block, 0, stream>>>(
+    select_kernel<EB, E, true, WD, K><<<grid, block, 0, stream>>>(
         ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
   } else {
-    select_kernel<EB, E, false, WPB, K><<<grid, block, 0, stream>>>(
+    select_kernel<EB, E, false, WD, K><<<grid, block, 0, stream>>>(
         ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
   }
   return hipGetLastError();
 }
 
-// Launch shape measured on MI355X over 2^28 elements: four waves of sixteen
-// loads (64 KiB of payload per tile, staged through 64 KiB of LDS) beat
-// smaller tiles, whose extra look-backs cost more than their occupancy gains.
+// Launch shape measured on MI355X over 2^28 f32 elements (us at p = 0.01 /
+// 0.5 / 0.99): 3 data waves x 12 loads, staged through 48 KiB of LDS,
+// 402 / 466 / 556; 3 x 16: 426 / 486 / 537; 7 x 8: 468 / 510 / 597.  Storing
+// straight from registers instead of staging wins at low selectivity (328 us
+// at p = 0.01) but loses at high (620 us at p = 0.99), so stores are staged.
 template <int EB>
 static hipError_t launch_sel_t(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                                int64_t n, void* scratch, hipStream_t stream) {
-  return launch_sel_cfg<EB, 4, 16>(in, flags, out, num_out, n, scratch, stream);
+  return launch_sel_cfg<EB, 3, 12>(in, flags, out, num_out, n, scratch, stream);
 }
 
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
