@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAMES] [--no-cpu]
 
 A step is one call of the library on one batch of synthetic input resident in
-HBM.  The headline step is the row-wise exclusive add scan of a bf16
+HBM; the K timed steps are captured once into a HIP graph and replayed (pass
+--eager to issue them one by one).  The headline step is the row-wise exclusive add scan of a bf16
 [8192, 8192] array (N(0,1), seed 1; float32 accumulation, bf16 output rounded
 to nearest even).  Consecutive steps rotate over several input/output buffer
 pairs so that no step finds its data in the 256 MB Infinity Cache left there
@@ -51,6 +52,8 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=4, help="buffer sets rotated between steps")
     ap.add_argument("--only", default="", help="comma-separated workload names to run (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue the timed calls one by one instead of replaying a HIP graph")
     return ap.parse_args()
 
 
@@ -119,7 +122,6 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
     sc.lib()
     only = set(filter(None, args.only.split(",")))
 
@@ -129,31 +131,46 @@ def main():
     def timed(launch, steps, warmup):
         """Time `steps` calls of launch(i) after `warmup` untimed ones.
 
-        Returns (wall seconds, per-launch kernel ms list).  The timed region is
-        bracketed by synchronizations; the calls inside it are enqueued back to
-        back with one pair of HIP events around the whole region on the launch
-        stream, and a second pass brackets each call with its own event pair.
-        The per-call figure is the smaller of the window average and the mean of
-        the per-call pairs (both include some launch overhead on the GPU).
+        Returns (wall seconds, per-call kernel ms list).  The timed region is
+        bracketed by synchronizations and holds the `steps` calls back to back:
+        captured once into a HIP graph and replayed (so host-side launch cost
+        does not stretch short kernels), or issued one by one with --eager.
+        One pair of HIP events on the launch stream brackets the region; a
+        second, eager pass brackets each call with its own pair of events.
+        The per-call figure is the smaller of the region average and the mean
+        of the per-call pairs (both include some dispatch overhead).
         """
         for i in range(warmup):
             launch(i)
         torch.cuda.synchronize()
+        graph = None
+        if not args.eager:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(steps):
+                    launch(i)
+            graph.replay()
+            torch.cuda.synchronize()
         w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
         t0 = time.perf_counter()
-        w0.record(stream)
-        for i in range(steps):
-            launch(i)
-        w1.record(stream)
+        w0.record(cur)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                launch(i)
+        w1.record(cur)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         window_ms = w0.elapsed_time(w1) / steps
+        del graph
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         for i in range(steps):
-            ev0[i].record(stream)
+            ev0[i].record(cur)
             launch(i)
-            ev1[i].record(stream)
+            ev1[i].record(cur)
         torch.cuda.synchronize()
         per = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
         if window_ms < float(np.mean(per)):
@@ -272,7 +289,7 @@ def main():
         def cp(i):
             rc = cl.copy_ceiling_copy16(ctypes.c_void_p(srcs[i % args.sets].data_ptr()),
                                         ctypes.c_void_p(dsts[i % args.sets].data_ptr()), half,
-                                        ctypes.c_void_p(stream.cuda_stream))
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
             assert rc == 0, rc
         wall, per = timed(cp, args.steps, args.warmup)
         copy = record("copy16", half // 2, head_bytes, wall, per, args.steps,
