@@ -43,8 +43,9 @@ KERNEL_SOURCES = {           # sources whose change invalidates stored counter r
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/pmc_traffic.json from the counter_collection.csv files of "
-                         "two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) and exit")
+                    help="merge into profiles/pmc_traffic.json the counter_collection.csv files "
+                         "of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--pmc-command", default="", help="the profiled command, recorded with --pmc-summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
@@ -65,14 +66,19 @@ def sources_sha(kind):
     return h.hexdigest()[:16]
 
 
-KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> workload key
-    "void sca::scan_rows_kernel<sca::FmtBF16, (sca::Op)0, true, 8, 4, 4>(": "rows_bf16_excl",
-    "(anonymous namespace)::copy16_kernel": "copy16",
+KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (workload, sources)
+    "void sca::scan_rows_kernel<sca::FmtBF16, (sca::Op)0, true, 8, 4, 4>(": ("rows_bf16_excl",
+                                                                           "scan_rows"),
+    "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, 4, 7, 16>(": ("dev_i32_add",
+                                                                       "scan_device"),
+    "void sca::select_kernel<4, 4, true, 3, 12>(": ("select_p0.5", "select"),
+    "(anonymous namespace)::copy16_kernel": ("copy16", None),
 }
 
 
 def pmc_summary(fetch_csv, write_csv, command):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel -> profiles/pmc_traffic.json."""
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, merged into
+    profiles/pmc_traffic.json (kernels absent from these CSVs keep their entries)."""
     import csv
 
     def read(path, counter):
@@ -82,31 +88,53 @@ def pmc_summary(fetch_csv, write_csv, command):
                 if row.get("Counter_Name") != counter:
                     continue
                 name = row["Kernel_Name"]
-                for prefix, key in KERNEL_KEYS.items():
+                for prefix, (key, _) in KERNEL_KEYS.items():
                     if name.startswith(prefix):
                         acc.setdefault(key, []).append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
-    out = {"command": command,
-           "note": "KiB per dispatch, averaged over dispatches; copy16 moved bytes/2 each way",
-           "copy16": {"bytes": 268435456, "fetch_kib": fetch["copy16"],
-                      "write_kib": write["copy16"]},
-           "kernels": {"rows_bf16_excl": {"fetch_kib": fetch["rows_bf16_excl"],
-                                          "write_kib": write["rows_bf16_excl"],
-                                          "source_sha": sources_sha("scan_rows")}}}
+    out = {"note": "KiB per dispatch, averaged over dispatches; copy16 moved bytes/2 each way",
+           "copy16": {}, "kernels": {}}
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as fh:
+            out.update(json.load(fh))
+    out["copy16"] = {"bytes": 268435456, "fetch_kib": fetch["copy16"],
+                     "write_kib": write["copy16"], "command": command}
+    for prefix, (key, kind) in KERNEL_KEYS.items():
+        if kind and key in fetch and key in write:
+            out["kernels"][key] = {"fetch_kib": fetch[key], "write_kib": write[key],
+                                   "source_sha": sources_sha(kind), "command": command,
+                                   "copy16": dict(out["copy16"])}
+    out.pop("command", None)
     with open(PMC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
 
+def traffic_bytes(key, kind):
+    """HBM bytes per launch from the stored counter readings, scaled by what the
+    same counters read for copy16; None if absent or the kernel changed since."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    try:
+        with open(PMC_FILE) as fh:
+            pm = json.load(fh)
+        k = pm["kernels"].get(key)
+        if not k or k.get("source_sha") != sources_sha(kind):
+            return None
+        c = k.get("copy16", pm["copy16"])
+        fr = c["bytes"] / 2 / (c["fetch_kib"] * 1024)     # bytes per counted byte
+        fw = c["bytes"] / 2 / (c["write_kib"] * 1024)
+        return k["fetch_kib"] * 1024 * fr + k["write_kib"] * 1024 * fw
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
 def main():
     args = parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary,
-                    command="rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -- python "
-                            "bench.py --only rows_bf16_excl,copy16 --steps 5 --warmup 1 --sets 1 "
-                            "--no-cpu")
+        pmc_summary(*args.pmc_summary[:2], command=args.pmc_command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the library has no multi-GPU "
@@ -321,18 +349,12 @@ def main():
                "cpu": platform.processor() or platform.machine()}
 
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
-    traffic = None
-    if os.path.exists(PMC_FILE):
-        try:
-            pm = json.load(open(PMC_FILE))
-            k = pm["kernels"].get("rows_bf16_excl")
-            c = pm["copy16"]
-            if k and k.get("source_sha") == sources_sha("scan_rows"):
-                fr = c["bytes"] / 2 / (c["fetch_kib"] * 1024)     # bytes per counted byte
-                fw = c["bytes"] / 2 / (c["write_kib"] * 1024)
-                traffic = k["fetch_kib"] * 1024 * fr + k["write_kib"] * 1024 * fw
-        except (KeyError, ValueError, ZeroDivisionError):
-            traffic = None
+    traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
+    for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select")):
+        t = traffic_bytes(key, kind)
+        if key in results and t is not None:
+            results[key]["traffic_bytes"] = t
+            results[key]["traffic_over_algorithmic"] = t / results[key]["algorithmic_bytes"]
 
     props = torch.cuda.get_device_properties(dev)
     line = {
