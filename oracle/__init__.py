@@ -15,6 +15,12 @@ computes, with the passages it follows:
   ``out[i] = p[i]``, applied to every row of a ``[rows, n]`` array (the row
   definitions of metaltile-std ``src/mlx/scan.rs``, header comment).  The
   identities are those of the "Algorithms" page, "Common conventions".
+* ``scan`` with ``op="mul"``: the product scans of metaltile-std
+  ``src/mlx/scan.rs`` ("Inclusive product scan", "Exclusive product scan";
+  identity 1 from its "Multi-op scan variants" table), accumulated in double.
+* ``reduce``: ``out[0] = op(x[0..n))`` per the "Algorithms" page, section
+  ``qd.algorithms.reduce_{add,min,max}``: the final state of the same
+  recurrence, the identity for an empty input.
 * ``select``: stream compaction per the "Algorithms" page, section
   ``qd.algorithms.select`` (stable, dense prefix, count).
 * ``f32_to_bf16`` / ``f32_to_f16`` and the widenings: round-to-nearest-even per
@@ -36,7 +42,7 @@ SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 # the oracle's own codes (see oracle.c); the product library has separate ones
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3, "i32": 4, "u32": 5, "i64": 6, "u64": 7}
-OPS = {"add": 0, "min": 1, "max": 2}
+OPS = {"add": 0, "min": 1, "max": 2, "mul": 3}
 # numpy storage type of each dtype (bf16 and f16 travel as raw uint16 bits)
 STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "f64": np.float64,
            "i32": np.int32, "u32": np.uint32, "i64": np.int64, "u64": np.uint64}
@@ -65,6 +71,8 @@ def lib():
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.oracle_scan.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp]
         L.oracle_scan.restype = i32
+        L.oracle_reduce.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        L.oracle_reduce.restype = i32
         L.oracle_select.argtypes = [vp, vp, vp, i64, i64]
         L.oracle_select.restype = i64
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -108,6 +116,26 @@ def scan(x, dtype, op="add", exclusive=False, want_ref=False):
         raise ValueError("oracle_scan rejected its arguments")
     if want_ref:
         return out, ref, absref
+    return out
+
+
+def reduce(x, dtype, op="add", want_ref=False):
+    """Fold all of the 1-D ``x`` (storage type of ``dtype``) from the identity.
+
+    Returns a one-element array of the storage type; with ``want_ref`` also
+    ``(ref, absref)`` as Python floats: the double accumulator (floating add
+    and mul; the value itself otherwise) and ``sum |x_j|``.
+    """
+    x = np.ascontiguousarray(x, dtype=STORAGE[dtype]).ravel()
+    out = np.zeros(1, dtype=STORAGE[dtype])
+    ref = np.zeros(1, dtype=np.float64)
+    absref = np.zeros(1, dtype=np.float64)
+    rc = lib().oracle_reduce(_ptr(x), _ptr(out), x.shape[0], DTYPES[dtype], OPS[op],
+                             _ptr(ref), _ptr(absref))
+    if rc != 0:
+        raise ValueError("oracle_reduce rejected its arguments")
+    if want_ref:
+        return out, float(ref[0]), float(absref[0])
     return out
 
 

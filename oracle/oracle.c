@@ -17,7 +17,10 @@
  *    The seed is the identity of (op, dtype) from the "Algorithms" page
  *    (Quadrants user guide), section "Common conventions", paragraph on the
  *    identity value: add 0; min +inf / INT_MAX / UINT_MAX; max -inf /
- *    INT_MIN / 0.
+ *    INT_MIN / 0.  The product (mul) has identity 1, per the op table of
+ *    metaltile-std src/mlx/scan.rs, comment "Multi-op scan variants", and
+ *    the definitions under "Inclusive product scan" / "Exclusive product
+ *    scan" there (out[i] = v[0]*...*v[i]; exclusive out[0] = 1).
  *  - Row-wise scans along the last axis of a contiguous [rows, n] array as
  *    defined in the header comment of metaltile-std src/mlx/scan.rs
  *    (inclusive out[i] = sum_{j<=i}, exclusive out[i] = sum_{j<i}, out[0]=0),
@@ -25,11 +28,16 @@
  *  - Stream compaction as defined on the "Algorithms" page, section
  *    qd.algorithms.select: every element whose flag is set is copied, in
  *    input order, into a dense prefix of out, and the count is returned.
+ *  - Reduction as defined on the "Algorithms" page, section
+ *    qd.algorithms.reduce_{add,min,max}: out[0] = op over in[0..n), here
+ *    the final state p[n] of the recurrence above (p[0], the identity, for
+ *    an empty input: "Tile operations and reductions" names the seed as the
+ *    final state of an empty scan).
  *
  * Arithmetic choices (each a reading of the pages, restated in the tests):
  *  - integer add is done in the unsigned type of the same width, so it wraps
  *    modulo 2^w (two's complement), with no signed-overflow UB;
- *  - floating add is accumulated in double, sequentially, and rounded once
+ *  - floating add and mul are accumulated in double, sequentially, and rounded once
  *    per output element: to float by a C cast (round to nearest even under
  *    the default FP environment), then, for bf16/f16 outputs, from that float
  *    to 16 bits by round-to-nearest-even written out below from the bit
@@ -43,7 +51,7 @@
  *    NaN payloads survive.
  *
  * Extra outputs for tolerance checks: ref[i] is the double accumulator of the
- * fold that produced out[i] (floating add only) and absref[i] is
+ * fold that produced out[i] (floating add and mul) and absref[i] is
  * sum_{j<=i} |x_j| in double.
  */
 #include <stdint.h>
@@ -54,7 +62,7 @@
 enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2, O_F64 = 3,
        O_I32 = 4, O_U32 = 5, O_I64 = 6, O_U64 = 7 };
 /* op codes of this oracle */
-enum { O_ADD = 0, O_MIN = 1, O_MAX = 2 };
+enum { O_ADD = 0, O_MIN = 1, O_MAX = 2, O_MUL = 3 };
 
 /* ---- 16-bit float conversions, from the bit patterns ---------------------- */
 
@@ -148,45 +156,94 @@ static void store_fp(void* p, int64_t i, int dt, double v) {
     }
 }
 
+/* ---- the combine, per value class ------------------------------------------ */
+
+/* a is the earlier operand.  Floating add and mul accumulate in double (the
+ * caller holds the double accumulator); min/max compare+select in the
+ * element's own type. */
+static double comb_fp64(int op, double a, double b) {
+    switch (op) {
+    case O_ADD: return a + b;
+    case O_MUL: return a * b;
+    case O_MIN: return (a < b) ? a : b;
+    default: return (a > b) ? a : b;
+    }
+}
+
+static float comb_fp32_minmax(int op, float a, float b) {
+    return (op == O_MIN) ? ((a < b) ? a : b) : ((a > b) ? a : b);
+}
+
+static uint32_t comb_u32(int dt, int op, uint32_t a, uint32_t b) {
+    if (op == O_ADD) return a + b;                        /* wraps mod 2^32 */
+    if (op == O_MUL) return a * b;                        /* wraps mod 2^32 */
+    if (dt == O_I32) {
+        int32_t x = (int32_t)a, y = (int32_t)b;
+        return (uint32_t)((op == O_MIN) ? ((x < y) ? x : y) : ((x > y) ? x : y));
+    }
+    return (op == O_MIN) ? ((a < b) ? a : b) : ((a > b) ? a : b);
+}
+
+static uint64_t comb_u64(int dt, int op, uint64_t a, uint64_t b) {
+    if (op == O_ADD) return a + b;                        /* wraps mod 2^64 */
+    if (op == O_MUL) return a * b;                        /* wraps mod 2^64 */
+    if (dt == O_I64) {
+        int64_t x = (int64_t)a, y = (int64_t)b;
+        return (uint64_t)((op == O_MIN) ? ((x < y) ? x : y) : ((x > y) ? x : y));
+    }
+    return (op == O_MIN) ? ((a < b) ? a : b) : ((a > b) ? a : b);
+}
+
+/* identities, as bit patterns of the element's width */
+static double ident_fp(int op) {
+    switch (op) {
+    case O_ADD: return 0.0;
+    case O_MUL: return 1.0;
+    case O_MIN: return INFINITY;
+    default: return -INFINITY;
+    }
+}
+
+static uint32_t ident_u32(int dt, int op) {
+    if (op == O_ADD) return 0u;
+    if (op == O_MUL) return 1u;
+    if (dt == O_I32) return (op == O_MIN) ? (uint32_t)INT32_MAX : (uint32_t)INT32_MIN;
+    return (op == O_MIN) ? UINT32_MAX : 0u;
+}
+
+static uint64_t ident_u64(int dt, int op) {
+    if (op == O_ADD) return 0u;
+    if (op == O_MUL) return 1u;
+    if (dt == O_I64) return (op == O_MIN) ? (uint64_t)INT64_MAX : (uint64_t)INT64_MIN;
+    return (op == O_MIN) ? UINT64_MAX : 0u;
+}
+
 /* ---- the fold ------------------------------------------------------------- */
 
-/* Floating fold over one fiber.  add accumulates in double; min/max keep the
- * earlier-operand-left compare+select on the element values (float for the
- * 32- and 16-bit formats, double for f64). */
+/* Floating fold over one fiber.  add and mul accumulate in double; min/max
+ * keep the earlier-operand-left compare+select on the element values (float
+ * for the 32- and 16-bit formats, double for f64). */
 static void fold_fp(const void* in, void* out, int64_t base, int64_t n, int dt, int op,
                     int exclusive, double* ref, double* absref) {
     double absacc = 0.0;
-    if (op == O_ADD) {
-        double acc = 0.0;                                  /* identity of add */
+    if (op == O_ADD || op == O_MUL || dt == O_F64) {
+        double acc = ident_fp(op);
         for (int64_t k = 0; k < n; ++k) {
             double x = load_fp(in, base + k, dt);
             absacc += fabs(x);
             if (exclusive) { store_fp(out, base + k, dt, acc); if (ref) ref[base + k] = acc; }
-            acc = acc + x;
+            acc = comb_fp64(op, acc, x);
             if (!exclusive) { store_fp(out, base + k, dt, acc); if (ref) ref[base + k] = acc; }
             if (absref) absref[base + k] = absacc;
         }
         return;
     }
-    if (dt == O_F64) {
-        double acc = (op == O_MIN) ? INFINITY : -INFINITY;
-        for (int64_t k = 0; k < n; ++k) {
-            double x = ((const double*)in)[base + k];
-            absacc += fabs(x);
-            if (exclusive) ((double*)out)[base + k] = acc;
-            acc = (op == O_MIN) ? ((acc < x) ? acc : x) : ((acc > x) ? acc : x);
-            if (!exclusive) ((double*)out)[base + k] = acc;
-            if (ref) ref[base + k] = exclusive ? ((double*)out)[base + k] : acc;
-            if (absref) absref[base + k] = absacc;
-        }
-        return;
-    }
-    float acc = (op == O_MIN) ? INFINITY : -INFINITY;
+    float acc = (float)ident_fp(op);
     for (int64_t k = 0; k < n; ++k) {
         float x = (float)load_fp(in, base + k, dt);        /* exact widening */
         absacc += fabs((double)x);
         if (exclusive) store_fp(out, base + k, dt, (double)acc);
-        acc = (op == O_MIN) ? ((acc < x) ? acc : x) : ((acc > x) ? acc : x);
+        acc = comb_fp32_minmax(op, acc, x);
         if (!exclusive) store_fp(out, base + k, dt, (double)acc);
         if (ref) ref[base + k] = (double)(exclusive ? (float)load_fp(out, base + k, dt) : acc);
         if (absref) absref[base + k] = absacc;
@@ -196,42 +253,22 @@ static void fold_fp(const void* in, void* out, int64_t base, int64_t n, int dt, 
 /* Integer fold over one fiber, in the unsigned type of the element's width. */
 static void fold_int(const void* in, void* out, int64_t base, int64_t n, int dt, int op,
                      int exclusive) {
-    if (dt == O_I32 || dt == O_U32) {
+    if (elem_size(dt) == 4) {
         const uint32_t* x = (const uint32_t*)in + base;
         uint32_t* y = (uint32_t*)out + base;
-        uint32_t acc;
-        if (op == O_ADD) acc = 0u;
-        else if (dt == O_I32) acc = (op == O_MIN) ? (uint32_t)INT32_MAX : (uint32_t)INT32_MIN;
-        else acc = (op == O_MIN) ? UINT32_MAX : 0u;
+        uint32_t acc = ident_u32(dt, op);
         for (int64_t k = 0; k < n; ++k) {
-            uint32_t v = x[k];
             if (exclusive) y[k] = acc;
-            if (op == O_ADD) acc = acc + v;               /* wraps mod 2^32 */
-            else if (dt == O_I32) {
-                int32_t a = (int32_t)acc, b = (int32_t)v;
-                acc = (uint32_t)((op == O_MIN) ? ((a < b) ? a : b) : ((a > b) ? a : b));
-            } else {
-                acc = (op == O_MIN) ? ((acc < v) ? acc : v) : ((acc > v) ? acc : v);
-            }
+            acc = comb_u32(dt, op, acc, x[k]);
             if (!exclusive) y[k] = acc;
         }
     } else {
         const uint64_t* x = (const uint64_t*)in + base;
         uint64_t* y = (uint64_t*)out + base;
-        uint64_t acc;
-        if (op == O_ADD) acc = 0u;
-        else if (dt == O_I64) acc = (op == O_MIN) ? (uint64_t)INT64_MAX : (uint64_t)INT64_MIN;
-        else acc = (op == O_MIN) ? UINT64_MAX : 0u;
+        uint64_t acc = ident_u64(dt, op);
         for (int64_t k = 0; k < n; ++k) {
-            uint64_t v = x[k];
             if (exclusive) y[k] = acc;
-            if (op == O_ADD) acc = acc + v;               /* wraps mod 2^64 */
-            else if (dt == O_I64) {
-                int64_t a = (int64_t)acc, b = (int64_t)v;
-                acc = (uint64_t)((op == O_MIN) ? ((a < b) ? a : b) : ((a > b) ? a : b));
-            } else {
-                acc = (op == O_MIN) ? ((acc < v) ? acc : v) : ((acc > v) ? acc : v);
-            }
+            acc = comb_u64(dt, op, acc, x[k]);
             if (!exclusive) y[k] = acc;
         }
     }
@@ -241,11 +278,55 @@ static void fold_int(const void* in, void* out, int64_t base, int64_t n, int dt,
  * Returns 0 on success, -1 for an unknown dtype/op. ref/absref may be NULL. */
 int oracle_scan(const void* in, void* out, int64_t rows, int64_t n, int dtype, int op,
                 int exclusive, double* ref, double* absref) {
-    if (elem_size(dtype) == 0 || op < O_ADD || op > O_MAX || rows < 0 || n < 0) return -1;
+    if (elem_size(dtype) == 0 || op < O_ADD || op > O_MUL || rows < 0 || n < 0) return -1;
     for (int64_t r = 0; r < rows; ++r) {
         if (is_float(dtype)) fold_fp(in, out, r * n, n, dtype, op, exclusive, ref, absref);
         else fold_int(in, out, r * n, n, dtype, op, exclusive);
     }
+    return 0;
+}
+
+/* Reduction of a flat array: out[0] = op-fold of in[0..n) from the identity,
+ * i.e. the final state of the same recurrence (an empty input leaves the
+ * identity).  ref/absref (may be NULL) receive the double accumulator
+ * (floating add/mul; the value itself otherwise) and sum |x| in double.
+ * Returns 0 on success, -1 for an unknown dtype/op. */
+int oracle_reduce(const void* in, void* out, int64_t n, int dtype, int op, double* ref,
+                  double* absref) {
+    if (elem_size(dtype) == 0 || op < O_ADD || op > O_MUL || n < 0) return -1;
+    double absacc = 0.0;
+    if (is_float(dtype) && (op == O_ADD || op == O_MUL || dtype == O_F64)) {
+        double acc = ident_fp(op);
+        for (int64_t k = 0; k < n; ++k) {
+            double x = load_fp(in, k, dtype);
+            absacc += fabs(x);
+            acc = comb_fp64(op, acc, x);
+        }
+        store_fp(out, 0, dtype, acc);
+        if (ref) *ref = acc;
+    } else if (is_float(dtype)) {
+        float acc = (float)ident_fp(op);
+        for (int64_t k = 0; k < n; ++k) {
+            float x = (float)load_fp(in, k, dtype);
+            absacc += fabs((double)x);
+            acc = comb_fp32_minmax(op, acc, x);
+        }
+        store_fp(out, 0, dtype, (double)acc);
+        if (ref) *ref = (double)acc;
+    } else if (elem_size(dtype) == 4) {
+        const uint32_t* x = (const uint32_t*)in;
+        uint32_t acc = ident_u32(dtype, op);
+        for (int64_t k = 0; k < n; ++k) acc = comb_u32(dtype, op, acc, x[k]);
+        *(uint32_t*)out = acc;
+        if (ref) *ref = (dtype == O_I32) ? (double)(int32_t)acc : (double)acc;
+    } else {
+        const uint64_t* x = (const uint64_t*)in;
+        uint64_t acc = ident_u64(dtype, op);
+        for (int64_t k = 0; k < n; ++k) acc = comb_u64(dtype, op, acc, x[k]);
+        *(uint64_t*)out = acc;
+        if (ref) *ref = (dtype == O_I64) ? (double)(int64_t)acc : (double)acc;
+    }
+    if (absref) *absref = absacc;
     return 0;
 }
 

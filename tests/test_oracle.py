@@ -71,6 +71,7 @@ def test_page_reduce_example(golden):
     for op in ("add", "min", "max"):
         inc = oracle.scan(x, "i32", op, exclusive=False)
         assert int(inc[-1]) == g[op], op           # the inclusive scan ends in the reduction
+        assert int(oracle.reduce(x, "i32", op)[0]) == g[op], op
 
 
 def test_page_select_example(golden):
@@ -89,8 +90,10 @@ def test_page_order_example(golden):
 
 def test_identities(golden):
     g = golden("identities.json")
-    for op in ("add", "min", "max"):
+    for op in ("add", "min", "max", "mul"):
         for dt in ALL_DT:
+            if dt not in g[op]:
+                continue
             x = random_input(dt, 3, 11)
             excl = oracle.scan(x, dt, op, exclusive=True)
             want = g[op][dt]
@@ -384,3 +387,141 @@ def test_select_keeps_nan_payloads():
     x = np.array([0x7fc00001, 0xffa00002, 0x3f800000], dtype=np.uint32).view(np.float32)
     out, k = oracle.select(x, np.array([1, 1, 0], np.uint8))
     assert k == 2 and out[:2].view(np.uint32).tolist() == [0x7fc00001, 0xffa00002]
+
+
+# ---- product scans ("mul") ---------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "bf16", "f16"])
+def test_prod_powers_of_two_exact(dt):
+    """x = 2 everywhere: the inclusive prefix is 2^(i+1), the exclusive 2^i (exact)."""
+    n = 15 if dt == "f16" else 100                 # stay inside each format's range
+    x = np.full(n, 2.0, np.float32)
+    xs = x.astype(np.float64) if dt == "f64" else (x if dt == "f32" else f32_to_bits(x, dt))
+    inc = as_float(oracle.scan(xs, dt, "mul"), dt)
+    exc = as_float(oracle.scan(xs, dt, "mul", exclusive=True), dt)
+    assert np.array_equal(inc, 2.0 ** np.arange(1, n + 1))
+    assert np.array_equal(exc, 2.0 ** np.arange(0, n))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_prod_signs_and_alternation(dt):
+    rng = np.random.default_rng(7)
+    s = rng.choice([-1.0, 1.0], size=300).astype(np.float32)
+    got = as_float(oracle.scan(f32_to_bits(s, dt) if dt != "f32" else s, dt, "mul"), dt)
+    # the sign of a product of +-1 is (-1)^(number of negatives so far)
+    want = np.where(np.cumsum(s < 0) % 2 == 1, -1.0, 1.0)
+    assert np.array_equal(got, want)
+    alt = np.tile(np.array([2.0, 0.5], np.float32), 50)
+    got = as_float(oracle.scan(f32_to_bits(alt, dt) if dt != "f32" else alt, dt, "mul"), dt)
+    assert np.array_equal(got, np.tile([2.0, 1.0], 50))
+
+
+def test_prod_zero_absorbs():
+    x = np.array([3.0, -2.0, 0.0, 5.0, -7.0], np.float32)
+    inc = oracle.scan(x, "f32", "mul")
+    assert inc[:2].tolist() == [3.0, -6.0]
+    assert np.all(inc[2:] == 0.0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "bf16", "f16"])
+def test_prod_matches_numpy_accumulate(dt):
+    """Against numpy's sequential multiply.accumulate in float64, rounded once."""
+    rng = np.random.default_rng(21)
+    n = 4096
+    v = (rng.choice([-1.0, 1.0], size=n) * (1.0 + rng.uniform(-1 / 64, 1 / 64, size=n)))
+    if dt == "f64":
+        x = v.astype(np.float64)
+        xv = x
+    elif dt == "f32":
+        x = v.astype(np.float32)
+        xv = x.astype(np.float64)
+    else:
+        x = f32_to_bits(v.astype(np.float32), dt)
+        xv = bits_to_f32(x, dt).astype(np.float64)
+    acc = np.multiply.accumulate(xv)
+    got, ref, _ = oracle.scan(x, dt, "mul", want_ref=True)
+    assert np.array_equal(ref, acc)
+    if dt == "f64":
+        assert np.array_equal(got, acc)
+    elif dt == "f32":
+        assert np.array_equal(got, acc.astype(np.float32))
+    else:
+        assert np.array_equal(got, f32_to_bits(acc.astype(np.float32), dt))
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "i64", "u64"])
+def test_int_prod_wraps_like_numpy(dt):
+    rng = np.random.default_rng(5)
+    x = rng.integers(-50 if dt[0] == "i" else 0, 50, size=500).astype(INT_DT[dt])
+    with np.errstate(over="ignore"):
+        want = np.multiply.accumulate(x, dtype=INT_DT[dt])
+    assert np.array_equal(oracle.scan(x, dt, "mul"), want)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "bf16", "f16"])
+def test_prod_brute_force_tiny(dt):
+    """Each prefix recomputed with math.prod (sequential double products), rounded once."""
+    for n in range(0, 9):
+        x = random_input(dt, n, 300 + n)
+        xv = [float(v) for v in as_float(x, dt)]
+        inc = as_float(oracle.scan(x, dt, "mul"), dt)
+        exc = as_float(oracle.scan(x, dt, "mul", exclusive=True), dt)
+        for i in range(n):
+            wi = float(as_float(_round_to(dt, math.prod(xv[:i + 1])), dt)[0])
+            we = float(as_float(_round_to(dt, math.prod(xv[:i])), dt)[0])
+            assert inc[i] == wi and exc[i] == we, (dt, n, i)
+
+
+# ---- reduce -----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ALL_DT)
+@pytest.mark.parametrize("op", ["add", "min", "max"])
+def test_reduce_is_last_inclusive_prefix(dt, op):
+    """Two separately written loops of the oracle agree: reduce == inclusive[-1]."""
+    for n in (1, 2, 17, 1000):
+        x = random_input(dt, n, 40 + n)
+        red = oracle.reduce(x, dt, op)
+        inc = oracle.scan(x, dt, op)
+        assert red.tobytes() == inc[-1:].tobytes(), (dt, op, n)
+
+
+@pytest.mark.parametrize("dt", ALL_DT)
+def test_reduce_empty_is_identity(dt, golden):
+    g = golden("identities.json")
+    for op in ("add", "min", "max"):
+        red = oracle.reduce(np.zeros(0, oracle.STORAGE[dt]), dt, op)
+        want = g[op][dt]
+        if dt in oracle.FLOATS:
+            assert as_float(red, dt)[0] == float(want), (dt, op)
+        else:
+            assert int(red[0]) == int(want), (dt, op)
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "i64", "u64"])
+def test_reduce_int_matches_numpy(dt):
+    x = random_input(dt, 100000, 9)
+    with np.errstate(over="ignore"):
+        assert oracle.reduce(x, dt, "add")[0] == np.add.reduce(x, dtype=INT_DT[dt])
+    assert oracle.reduce(x, dt, "min")[0] == x.min()
+    assert oracle.reduce(x, dt, "max")[0] == x.max()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_reduce_fp_add_near_exact_sum(dt):
+    """The double fold is within n * 2^-53 * sum|x| of math.fsum's exact sum."""
+    x = random_input(dt, 200000, 13)
+    red, ref, absref = oracle.reduce(x, dt, "add", want_ref=True)
+    exact = math.fsum(float(v) for v in x)
+    assert abs(ref - exact) <= x.size * 2.0 ** -53 * absref
+    assert abs(absref - math.fsum(abs(float(v)) for v in x)) <= x.size * 2.0 ** -53 * absref
+    if dt == "f32":
+        assert red[0] == np.float32(ref)
+
+
+def test_reduce_minmax_signed_zero_takes_later(golden):
+    g = golden("tie_break.json")
+    for case in g["cases"]:
+        x = np.array([float(v) for v in case["input"]], dtype=np.float32)
+        red = oracle.reduce(x, "f32", case["op"])
+        want = np.array([float(case["inclusive"][-1])], dtype=np.float32)
+        assert red.view(np.uint32).tolist() == want.view(np.uint32).tolist(), case
