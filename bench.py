@@ -10,8 +10,9 @@ HBM; the K timed steps are captured once into a HIP graph and replayed (pass
 to nearest even).  Consecutive steps rotate over several input/output buffer
 pairs so that no step finds its data in the 256 MB Infinity Cache left there
 by the previous one.  The other workloads (row scans of fp32 [1024, 4096] and
-bf16 [8192, 8191], the device-wide scans and select) are timed the same way
-and reported inside the same JSON line under "workloads".
+bf16 [8192, 8191], the bf16 product scan, the device-wide exclusive and
+inclusive scans, the reductions and select) are timed the same way and
+reported inside the same JSON line under "workloads".
 
 Prints ONE JSON line.  "value" is elements/s of the headline workload (wall
 clock over the K timed steps); "roofline" rates the headline kernel by its
@@ -37,6 +38,7 @@ KERNEL_SOURCES = {           # sources whose change invalidates stored counter r
     "scan_rows": ["device.hpp", "scan_rows.hip"],
     "scan_device": ["device.hpp", "scan_device.hip"],
     "select": ["device.hpp", "select.hip"],
+    "reduce": ["device.hpp", "reduce.hip"],
 }
 
 
@@ -69,8 +71,9 @@ def sources_sha(kind):
 KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (workload, sources)
     "void sca::scan_rows_kernel<sca::FmtBF16, (sca::Op)0, true, 8, 4, 4>(": ("rows_bf16_excl",
                                                                            "scan_rows"),
-    "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, 4, 7, 16>(": ("dev_i32_add",
-                                                                       "scan_device"),
+    "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, false, 4, 7, 16>(": ("dev_i32_add",
+                                                                              "scan_device"),
+    "void sca::reduce_partials_kernel<sca::FmtI32, (sca::Op)0, 4>(": ("reduce_i32_add", "reduce"),
     "void sca::select_kernel<4, 4, true, 3, 12>(": ("select_p0.5", "select"),
     "(anonymous namespace)::copy16_kernel": ("copy16", None),
 }
@@ -283,6 +286,38 @@ def main():
                 record(name, x4.numel(), x4.numel() * x4.element_size() * 2, wall, per, K,
                        "includes the descriptor-reset fill kernel")
         del x4, y4
+    if want("rows_bf16_prod_excl"):
+        xp2 = wl.prod_rows_bf16(rows, n)
+        xs = [bf16_dev(xp2) for _ in range(args.sets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
+        wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "mul", True, ys[i % args.sets]),
+                          K, W)
+        record("rows_bf16_prod_excl", rows * n, head_bytes, wall, per, K,
+               "product scan, factors +-(1 + U[-1/64, 1/64)) in bf16, seed 12")
+        del xs, ys
+    if want("dev_i32_add_incl"):
+        n3 = wl.FULL["dev_i32"]
+        x3 = torch.from_numpy(wl.dev_i32()).to(dev)
+        y3 = torch.empty_like(x3)
+        s3 = torch.empty(sc.scan_device_scratch_bytes(n3, "i32"), dtype=torch.uint8, device=dev)
+        wall, per = timed(lambda i: sc.scan_device_inclusive(x3, "add", y3, s3), K, W)
+        record("dev_i32_add_incl", n3, n3 * 8, wall, per, K,
+               "inclusive form; includes the descriptor-reset fill kernel")
+        del x3, y3
+    red_cases = (("reduce_i32_add", "i32", "add"), ("reduce_f32_add", "f32", "add"),
+                 ("reduce_f32_min", "f32", "min"), ("reduce_i64_max", "i64", "max"))
+    for name, which, op in red_cases:
+        if not want(name):
+            continue
+        src = {"i32": wl.dev_i32, "f32": wl.dev_f32, "i64": wl.dev_i64}[which]()
+        x5 = torch.from_numpy(src).to(dev)
+        y5 = torch.empty(1, dtype=x5.dtype, device=dev)
+        s5 = torch.empty(max(16, sc.reduce_device_scratch_bytes(x5.numel(), which)),
+                         dtype=torch.uint8, device=dev)
+        wall, per = timed(lambda i: sc.reduce_device(x5, op, y5, s5), K, W)
+        record(name, x5.numel(), x5.numel() * x5.element_size(), wall, per, K,
+               "algorithmic bytes = n elements read; includes the one-wave final kernel")
+        del x5, y5
     nsel = wl.FULL["sel"]
     for p in wl.SELECT_P:
         name = f"select_p{p}"
@@ -350,7 +385,8 @@ def main():
 
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
     traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
-    for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select")):
+    for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select"),
+                      ("reduce_i32_add", "reduce")):
         t = traffic_bytes(key, kind)
         if key in results and t is not None:
             results[key]["traffic_bytes"] = t

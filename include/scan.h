@@ -1,7 +1,7 @@
 /*
  * scan.h - C ABI of the stream_compaction_amd library (libscan_amd.so):
- * row-wise prefix scan, device-wide exclusive scan and stream compaction on
- * one AMD Instinct MI355X (gfx950).
+ * row-wise prefix scan, device-wide exclusive and inclusive scan, device-wide
+ * reduction and stream compaction on one AMD Instinct MI355X (gfx950).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -32,7 +32,9 @@
  *    buffers.  Scratch must be 16-byte aligned.
  *  - Identities ("Algorithms" page, section "Common conventions", identity
  *    value): add 0; min +inf (floats) / INT32_MAX, INT64_MAX / UINT32_MAX,
- *    UINT64_MAX; max -inf (floats) / INT32_MIN, INT64_MIN / 0.
+ *    UINT64_MAX; max -inf (floats) / INT32_MIN, INT64_MIN / 0.  The product
+ *    (row scans only) has identity 1 (metaltile-std src/mlx/scan.rs, op table
+ *    of the "Multi-op scan variants" comment).
  *  - Combine order: the earlier operand is always on the left ("Tile
  *    operations and reductions", section "Why not just infer it from
  *    reduce?"); min is (a < b ? a : b) and max is (a > b ? a : b), so a tie
@@ -67,14 +69,16 @@ typedef enum {
     SCAN_I32 = 5, SCAN_U32 = 6, SCAN_I64 = 7, SCAN_U64 = 8
 } scan_dtype;
 
-typedef enum { SCAN_ADD = 1, SCAN_MIN = 2, SCAN_MAX = 3 } scan_op;
+typedef enum { SCAN_ADD = 1, SCAN_MIN = 2, SCAN_MAX = 3, SCAN_MUL = 4 } scan_op;
 
 /*
  * Row-wise scan along the last axis of a contiguous row-major [rows, n]
  * array (row r starts at element r*n).  Defined in the header comment of
  * metaltile-std src/mlx/scan.rs: inclusive out[r,i] = op(in[r,0..i]),
  * exclusive out[r,i] = op(in[r,0..i-1]) with out[r,0] = identity; its
- * "Multi-op scan variants" comment extends this to min and max.
+ * "Multi-op scan variants" comment extends this to prod, min and max, and its
+ * "Inclusive product scan" / "Exclusive product scan" sections define the
+ * product forms (out[r,i] = in[r,0] * ... * in[r,i]; exclusive out[r,0] = 1).
  *
  *   in, out    device pointers, [rows, n] of `dtype`, same layout; must not
  *              overlap.
@@ -84,7 +88,8 @@ typedef enum { SCAN_ADD = 1, SCAN_MIN = 2, SCAN_MAX = 3 } scan_op;
  *              output is rounded once to `dtype`, nearest-even ("Tile
  *              operations and reductions", section "Storage and arithmetic
  *              precision").
- *   op         SCAN_ADD, SCAN_MIN or SCAN_MAX.
+ *   op         SCAN_ADD, SCAN_MIN, SCAN_MAX or SCAN_MUL (products are formed
+ *              in float32 and rounded once per output, like sums).
  *   exclusive  0 = inclusive, 1 = exclusive (any other value: SCAN_EINVAL).
  *   rows, n    0 <= rows, n <= INT32_MAX.
  */
@@ -101,13 +106,47 @@ scan_status scan_rows(const void* in, void* out, int64_t rows, int64_t n,
  *   in, out    device pointers to n elements of `dtype`; must not overlap.
  *   dtype      SCAN_I32, SCAN_U32, SCAN_F32, SCAN_I64, SCAN_U64, SCAN_F64
  *              (the dtype set of that page's "Common conventions").
- *   op         SCAN_ADD, SCAN_MIN, SCAN_MAX.
+ *   op         SCAN_ADD, SCAN_MIN, SCAN_MAX (SCAN_MUL: SCAN_ENOTSUP).
  *   scratch    >= scan_device_scratch_bytes(n, dtype) bytes, 16-byte aligned,
  *              must not overlap in/out.
  */
 size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype);
 scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
                         void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Device-wide INCLUSIVE scan of a flat array: out[i] = op(in[0..i]).  The
+ * inclusive prefix sum of the "Algorithms" page's PrefixSumExecutor section
+ * (there in place, i32 and add only), here out of place with the dtypes, ops,
+ * scratch and errors of scan_device (same scratch size helper); equivalently
+ * the inclusive form of the row scan's definition applied to one row of n.
+ */
+scan_status scan_device_inclusive(const void* in, void* out, int64_t n, scan_dtype dtype,
+                                  scan_op op, void* scratch, size_t scratch_bytes,
+                                  void* stream);
+
+/*
+ * Device-wide reduction ("Algorithms" page, section
+ * qd.algorithms.reduce_{add,min,max}): out[0] = op(in[0..n)), written on the
+ * device.  n == 0 writes the identity (the seed, which "Tile operations and
+ * reductions" gives as the final state of an empty fiber).  Integer and
+ * min/max results equal the sequential left fold bit for bit (ties keep the
+ * later element); floating add is a fixed regrouping, deterministic for a
+ * given n and pointer alignment.
+ *
+ *   in         device pointer to n elements of `dtype`.
+ *   out        device pointer to one element of `dtype`; must not overlap in or
+ *              scratch.
+ *   dtype      SCAN_I32, SCAN_U32, SCAN_F32, SCAN_I64, SCAN_U64, SCAN_F64.
+ *   op         SCAN_ADD, SCAN_MIN, SCAN_MAX (SCAN_MUL: SCAN_ENOTSUP).
+ *   scratch    >= reduce_device_scratch_bytes(n, dtype) bytes, 16-byte
+ *              aligned, must not overlap in/out (may be NULL when that size is
+ *              0, i.e. n == 0).  Holds per-workgroup partials; needs no
+ *              initialization.
+ */
+size_t reduce_device_scratch_bytes(int64_t n, scan_dtype dtype);
+scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                          void* scratch, size_t scratch_bytes, void* stream);
 
 /*
  * Stream compaction ("Algorithms" page, section qd.algorithms.select): every

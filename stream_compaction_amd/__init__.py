@@ -9,12 +9,18 @@ fallback: if the library is missing or a call fails, an exception is raised.
 Entry points (same names as the C ABI):
 
 * ``scan_rows(x, op="add", exclusive=False, out=None)`` - scan along the last
-  axis of a contiguous ``[rows, n]`` float32/float16/bfloat16 tensor.
+  axis of a contiguous ``[rows, n]`` float32/float16/bfloat16 tensor
+  (op: add, min, max, mul).
 * ``scan_device(x, op="add", out=None, scratch=None)`` - device-wide exclusive
   scan of a 1-D int32/uint32/float32/int64/uint64/float64 tensor.
+* ``scan_device_inclusive(x, op="add", out=None, scratch=None)`` - the same,
+  inclusive.
+* ``reduce_device(x, op="add", out=None, scratch=None)`` - device-wide
+  reduction into a 1-element GPU tensor.
 * ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
   stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
-* ``scan_device_scratch_bytes(n, dtype)``, ``select_compact_scratch_bytes(n)``.
+* ``scan_device_scratch_bytes(n, dtype)``, ``reduce_device_scratch_bytes(n,
+  dtype)``, ``select_compact_scratch_bytes(n)``.
 """
 import ctypes
 import os
@@ -26,8 +32,9 @@ LIB_PATH = os.path.join(_HERE, "libscan_amd.so")
 _STATUS = {0: "SCAN_OK", 1: "SCAN_EINVAL", 2: "SCAN_ENOTSUP", 3: "SCAN_EALIAS",
            4: "SCAN_ESCRATCH", 5: "SCAN_EHIP"}
 DTYPE_CODES = {"f32": 1, "f16": 2, "bf16": 3, "f64": 4, "i32": 5, "u32": 6, "i64": 7, "u64": 8}
-OP_CODES = {"add": 1, "min": 2, "max": 3}
-EXPORTS = ("scan_rows", "scan_device", "scan_device_scratch_bytes", "select_compact",
+OP_CODES = {"add": 1, "min": 2, "max": 3, "mul": 4}
+EXPORTS = ("scan_rows", "scan_device", "scan_device_inclusive", "scan_device_scratch_bytes",
+           "reduce_device", "reduce_device_scratch_bytes", "select_compact",
            "select_compact_scratch_bytes", "scan_status_str", "scan_last_hip_error")
 
 _lib = None
@@ -58,6 +65,12 @@ def load(path):
     L.scan_device_scratch_bytes.restype = sz
     L.scan_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
     L.scan_device.restype = i32
+    L.scan_device_inclusive.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
+    L.scan_device_inclusive.restype = i32
+    L.reduce_device_scratch_bytes.argtypes = [i64, i32]
+    L.reduce_device_scratch_bytes.restype = sz
+    L.reduce_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
+    L.reduce_device.restype = i32
     L.select_compact_scratch_bytes.argtypes = [i64]
     L.select_compact_scratch_bytes.restype = sz
     L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
@@ -150,6 +163,15 @@ def scan_device_scratch_bytes(n, dtype):
 
 def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
     """Device-wide exclusive scan of the 1-D tensor ``x``."""
+    return _scan_device(lib().scan_device, x, op, out, scratch, stream, dtype)
+
+
+def scan_device_inclusive(x, op="add", out=None, scratch=None, stream=None, dtype=None):
+    """Device-wide inclusive scan of the 1-D tensor ``x``."""
+    return _scan_device(lib().scan_device_inclusive, x, op, out, scratch, stream, dtype)
+
+
+def _scan_device(fn, x, op, out, scratch, stream, dtype):
     torch = _torch()
     if x.dim() != 1:
         raise ValueError("x must be 1-D")
@@ -162,9 +184,33 @@ def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
     need = scan_device_scratch_bytes(n, name)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    check(lib().scan_device(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name],
-                            OP_CODES[op], _dev_ptr(scratch, "scratch"), scratch.numel(),
-                            _stream(stream)))
+    check(fn(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name], OP_CODES[op],
+             _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
+    return out
+
+
+def reduce_device_scratch_bytes(n, dtype):
+    name = dtype if isinstance(dtype, str) else dtype_name(dtype)
+    return int(lib().reduce_device_scratch_bytes(int(n), DTYPE_CODES[name]))
+
+
+def reduce_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
+    """Device-wide reduction of the 1-D tensor ``x`` into ``out`` (1 element, on the GPU)."""
+    torch = _torch()
+    if x.dim() != 1:
+        raise ValueError("x must be 1-D")
+    n = x.shape[0]
+    name = _name(x, dtype)
+    if out is None:
+        out = torch.empty(1, dtype=x.dtype, device=x.device)
+    if out.numel() != 1 or out.dtype != x.dtype:
+        raise ValueError("out must be one element of x's dtype")
+    need = reduce_device_scratch_bytes(n, name)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    check(lib().reduce_device(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name],
+                              OP_CODES[op], _dev_ptr(scratch, "scratch"), scratch.numel(),
+                              _stream(stream)))
     return out
 
 

@@ -29,6 +29,7 @@ int op_index(scan_op op) {
     case SCAN_ADD: return 0;
     case SCAN_MIN: return 1;
     case SCAN_MAX: return 2;
+    case SCAN_MUL: return 3;
   }
   return -1;
 }
@@ -96,14 +97,15 @@ size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype) {
   return round16(sca::scan_device_tiles(n, fmt) * sca::scan_device_desc_words(fmt) * 8);
 }
 
-scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
-                        void* scratch, size_t scratch_bytes, void* stream) {
+static scan_status scan_device_any(const void* in, void* out, int64_t n, scan_dtype dtype,
+                                   scan_op op, bool inclusive, void* scratch,
+                                   size_t scratch_bytes, void* stream) {
   sca::Fmt fmt;
   size_t eb;
   if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
   if (fmt == sca::Fmt::F16 || fmt == sca::Fmt::BF16) return SCAN_ENOTSUP;
   const int opi = op_index(op);
-  if (opi < 0) return SCAN_ENOTSUP;
+  if (opi < 0 || opi > 2) return SCAN_ENOTSUP;
   if (n < 0 || n > kMaxN) return SCAN_EINVAL;
   if (n == 0) return SCAN_OK;
   if (in == nullptr || out == nullptr || scratch == nullptr) return SCAN_EINVAL;
@@ -113,7 +115,48 @@ scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, 
   const size_t bytes = (size_t)n * eb;
   if (overlap(in, bytes, out, bytes)) return SCAN_EALIAS;
   if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes)) return SCAN_EALIAS;
-  return hip_status(sca::launch_scan_device(in, out, n, fmt, opi, scratch, (hipStream_t)stream));
+  return hip_status(
+      sca::launch_scan_device(in, out, n, fmt, opi, inclusive, scratch, (hipStream_t)stream));
+}
+
+scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                        void* scratch, size_t scratch_bytes, void* stream) {
+  return scan_device_any(in, out, n, dtype, op, false, scratch, scratch_bytes, stream);
+}
+
+scan_status scan_device_inclusive(const void* in, void* out, int64_t n, scan_dtype dtype,
+                                  scan_op op, void* scratch, size_t scratch_bytes,
+                                  void* stream) {
+  return scan_device_any(in, out, n, dtype, op, true, scratch, scratch_bytes, stream);
+}
+
+size_t reduce_device_scratch_bytes(int64_t n, scan_dtype dtype) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb) || n < 0) return 0;
+  return round16(sca::reduce_partials(n, fmt) * 8);
+}
+
+scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                          void* scratch, size_t scratch_bytes, void* stream) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
+  if (fmt == sca::Fmt::F16 || fmt == sca::Fmt::BF16) return SCAN_ENOTSUP;
+  const int opi = op_index(op);
+  if (opi < 0 || opi > 2) return SCAN_ENOTSUP;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
+  if (out == nullptr || !aligned(out, eb)) return SCAN_EINVAL;
+  const size_t need = reduce_device_scratch_bytes(n, dtype);
+  if (n > 0) {
+    if (in == nullptr || scratch == nullptr) return SCAN_EINVAL;
+    if (!aligned(in, eb) || !aligned(scratch, 16)) return SCAN_EINVAL;
+    if (scratch_bytes < need) return SCAN_ESCRATCH;
+    const size_t bytes = (size_t)n * eb;
+    if (overlap(in, bytes, out, eb)) return SCAN_EALIAS;
+    if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, eb)) return SCAN_EALIAS;
+  }
+  return hip_status(sca::launch_reduce(in, out, n, fmt, opi, scratch, (hipStream_t)stream));
 }
 
 size_t select_compact_scratch_bytes(int64_t n) {

@@ -25,8 +25,10 @@ constexpr int kWave = 64;
 // src/mlx/scan.rs do, so ties (e.g. +0 vs -0) yield the later operand; the
 // compiler keeps them as v_cmp + v_cndmask (no v_min/v_max, whose signed-zero
 // rules differ).  Integer add runs in the unsigned type: it wraps mod 2^w.
+// Mul (the product scans of the same page, identity 1) is defined for the
+// floating accumulation types only.
 // ---------------------------------------------------------------------------
-enum class Op : int { Add = 0, Min = 1, Max = 2 };
+enum class Op : int { Add = 0, Min = 1, Max = 2, Mul = 3 };
 
 template <class T> struct Limits;
 template <> struct Limits<float> {
@@ -57,6 +59,7 @@ template <> struct Limits<uint64_t> {
 template <Op O, class W>
 __device__ __forceinline__ W identity() {
   if constexpr (O == Op::Add) return W(0);
+  else if constexpr (O == Op::Mul) return W(1);
   else if constexpr (O == Op::Min) return Limits<W>::highest();
   else return Limits<W>::lowest();
 }
@@ -74,6 +77,9 @@ __device__ __forceinline__ W combine(W a, W b) {
       using U = typename Unsigned<W>::type;
       return (W)((U)a + (U)b);
     }
+  } else if constexpr (O == Op::Mul) {
+    static_assert(std::is_same_v<W, float> || std::is_same_v<W, double>, "product of floats only");
+    return a * b;
   } else if constexpr (O == Op::Min) {
     return (a < b) ? a : b;
   } else {

@@ -14,15 +14,21 @@ enum class Fmt : int { F32, F16, BF16, F64, I32, U32, I64, U64 };
 // Workgroup size of every kernel (four wave64s).
 constexpr int kBlock = 256;
 
-// Row-wise scan; op: 0 add, 1 min, 2 max.
+// Row-wise scan; op: 0 add, 1 min, 2 max, 3 mul (floating formats).
 hipError_t launch_scan_rows(const void* in, void* out, int64_t rows, int64_t n, Fmt fmt, int op,
                             bool exclusive, hipStream_t stream);
 
-// Device-wide exclusive scan.
+// Device-wide exclusive (or inclusive) scan; op: 0 add, 1 min, 2 max.
 size_t scan_device_tiles(int64_t n, Fmt fmt);       // descriptors needed
 size_t scan_device_desc_words(Fmt fmt);             // 64-bit words per descriptor
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
-                              void* scratch, hipStream_t stream);
+                              bool inclusive, void* scratch, hipStream_t stream);
+
+// Device-wide reduction into out[0]; op: 0 add, 1 min, 2 max.  n == 0 writes
+// the identity.  Scratch holds one partial per workgroup of the first launch.
+size_t reduce_partials(int64_t n, Fmt fmt);         // partials (8-byte slots) needed
+hipError_t launch_reduce(const void* in, void* out, int64_t n, Fmt fmt, int op, void* scratch,
+                         hipStream_t stream);
 
 // Stream compaction.
 size_t select_tiles(int64_t n, size_t elem_bytes);

@@ -1,7 +1,10 @@
 // Device-wide exclusive scan (add/min/max) in one pass over the data
 // ("Algorithms" page, Quadrants user guide: section
 // qd.algorithms.exclusive_scan_{add,min,max} for the contract, "Related" for
-// decoupled look-back as the alternative to a phase-per-launch staircase).
+// decoupled look-back as the alternative to a phase-per-launch staircase),
+// and its inclusive form (out[i] = op over in[0..i], the in-place prefix sum
+// of that page's PrefixSumExecutor section, here out of place and for every
+// dtype and op): the same kernel with a different store stage.
 //
 // Workgroup b owns tile b.  It has WD data waves and one look-back wave.
 //  - Each data wave loads its run of 64*K 16-byte vectors (load j of lane l
@@ -35,7 +38,7 @@ __device__ __forceinline__ uint32_t lds_acquire(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <class F, Op O, int E, int WD, int K>
+template <class F, Op O, bool INCL, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     uintptr_t in_base, uintptr_t out_base, int64_t n, int64_t ph, int64_t ntiles, uint64_t* desc) {
   using S = typename F::S;
@@ -101,9 +104,14 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     for (int j = 0; j < K; ++j) {
       const W q = combine<O>(wp, pre[j]);
       W y[E];
-      y[0] = q;
+      if constexpr (INCL) {
 #pragma unroll
-      for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(q, x[j][k]);
+      } else {
+        y[0] = q;
+#pragma unroll
+        for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
+      }
       const int64_t v = wb + j * kWave + lane;
       if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
     }
@@ -181,7 +189,7 @@ size_t scan_device_tiles(int64_t n, Fmt fmt) {
 
 // One launch shape: WD data waves (plus the look-back wave), K vectors per
 // lane per tile.
-template <class F, Op O, int WD, int K>
+template <class F, Op O, bool INCL, int WD, int K>
 static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
                                  hipStream_t stream) {
   using S = typename F::S;
@@ -198,10 +206,11 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   if (vec) {
-    scan_device_kernel<F, O, EV, WD, K><<<grid, block, 0, stream>>>(
+    scan_device_kernel<F, O, INCL, EV, WD, K><<<grid, block, 0, stream>>>(
         ia - ph * sizeof(S), oa - ph * sizeof(S), n, ph, ntiles, desc);
   } else {
-    scan_device_kernel<F, O, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles, desc);
+    scan_device_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles,
+                                                                        desc);
   }
   return hipGetLastError();
 }
@@ -211,30 +220,31 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
 // 4 x 16: 525, 3 x 8: 527.  Few, large tiles win: each tile's look-back costs
 // microseconds of latency, and registers (not LDS) bound the tile size.
 template <class F, Op O>
-static hipError_t launch_dev_t(const void* in, void* out, int64_t n, void* scratch,
+static hipError_t launch_dev_t(const void* in, void* out, int64_t n, bool incl, void* scratch,
                                hipStream_t stream) {
-  return launch_dev_cfg<F, O, 7, 16>(in, out, n, scratch, stream);
+  return incl ? launch_dev_cfg<F, O, true, 7, 16>(in, out, n, scratch, stream)
+              : launch_dev_cfg<F, O, false, 7, 16>(in, out, n, scratch, stream);
 }
 
 template <class F>
-static hipError_t launch_dev_f(const void* in, void* out, int64_t n, int op, void* scratch,
-                               hipStream_t stream) {
+static hipError_t launch_dev_f(const void* in, void* out, int64_t n, int op, bool incl,
+                               void* scratch, hipStream_t stream) {
   switch (op) {
-    case 0: return launch_dev_t<F, Op::Add>(in, out, n, scratch, stream);
-    case 1: return launch_dev_t<F, Op::Min>(in, out, n, scratch, stream);
-    default: return launch_dev_t<F, Op::Max>(in, out, n, scratch, stream);
+    case 0: return launch_dev_t<F, Op::Add>(in, out, n, incl, scratch, stream);
+    case 1: return launch_dev_t<F, Op::Min>(in, out, n, incl, scratch, stream);
+    default: return launch_dev_t<F, Op::Max>(in, out, n, incl, scratch, stream);
   }
 }
 
-hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op, void* scratch,
-                              hipStream_t stream) {
+hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
+                              bool inclusive, void* scratch, hipStream_t stream) {
   switch (fmt) {
-    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, scratch, stream);
-    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, scratch, stream);
-    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, scratch, stream);
-    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, scratch, stream);
-    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, scratch, stream);
-    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, scratch, stream);
+    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,7 @@
 // Row-wise inclusive/exclusive scan along the last axis of a contiguous
 // [rows, n] array (metaltile-std src/mlx/scan.rs: header comment for the
-// definitions, "Multi-op scan variants" for min/max and their identities).
+// definitions, "Multi-op scan variants" for prod/min/max and their identities,
+// "Inclusive product scan" / "Exclusive product scan" for the product).
 //
 // Mapping: one workgroup of WPR wave64s owns one row and walks it in chunks of
 // WPR*64*K vectors of a 16-byte-aligned window (so ragged rows, whose starts
@@ -164,8 +165,10 @@ static hipError_t launch_rows_f(const void* in, void* out, int64_t rows, int64_t
                         : launch_rows_t<F, Op::Add, false>(in, out, rows, n, stream);
     case 1: return excl ? launch_rows_t<F, Op::Min, true>(in, out, rows, n, stream)
                         : launch_rows_t<F, Op::Min, false>(in, out, rows, n, stream);
-    default: return excl ? launch_rows_t<F, Op::Max, true>(in, out, rows, n, stream)
-                         : launch_rows_t<F, Op::Max, false>(in, out, rows, n, stream);
+    case 2: return excl ? launch_rows_t<F, Op::Max, true>(in, out, rows, n, stream)
+                        : launch_rows_t<F, Op::Max, false>(in, out, rows, n, stream);
+    default: return excl ? launch_rows_t<F, Op::Mul, true>(in, out, rows, n, stream)
+                         : launch_rows_t<F, Op::Mul, false>(in, out, rows, n, stream);
   }
 }
 

@@ -9,6 +9,13 @@
   float32 bound above (the union covers prefixes that cancel towards zero,
   where one 16-bit ulp is finer than legitimate float32 regrouping error).
 * float64 add (outside the five workloads): |gpu - ref| <= 1e-12 * A_i + 1e-300.
+* products (row scans, float32 accumulation): a product of m factors formed
+  with m - 1 float32 roundings, in any grouping, is within
+  gamma = (m-1)u / (1 - (m-1)u) (u = 2^-24) of the exact product relative to
+  it; the oracle's double product adds at most m * 2^-53.  The check is
+  |gpu - ref| <= 1.01 * (gamma + m 2^-52) |ref|, plus half an output ulp
+  (at the GPU's value) for bf16/f16 outputs, which are rounded once from the
+  float32 product.
 """
 import numpy as np
 import torch
@@ -75,3 +82,30 @@ def check_exact(gpu, ora, label=""):
         i = diff[0]
         raise AssertionError(f"{label}: {diff.size} of {gpu.size} elements differ; first at "
                              f"flat index {i}: gpu={gpu.ravel()[i]!r} oracle={ora.ravel()[i]!r}")
+
+
+def check_fp_mul(gpu, ref, m, dtype, label=""):
+    """Assert the product bound; m[i] = number of factors behind output i.
+
+    Returns the largest error as a fraction of its bound.
+    """
+    gpu = np.asarray(gpu)
+    g = decode16(gpu, dtype) if dtype in ("bf16", "f16") else gpu.astype(np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    k = np.maximum(m - 1, 0)
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    bound = 1.01 * (gamma + m * 2.0 ** -52) * np.abs(ref)
+    if dtype in ("bf16", "f16"):
+        bound = bound + 0.5 * ulp16(g, dtype)
+    err = np.abs(g - ref)
+    ok = err <= bound
+    if not ok.all():
+        bad = np.flatnonzero(~ok.ravel())
+        i = bad[0]
+        raise AssertionError(
+            f"{label}: {bad.size} of {ok.size} outputs out of tolerance; first at flat index {i}: "
+            f"gpu={g.ravel()[i]!r} ref={ref.ravel()[i]!r} m={m.ravel()[i]!r}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(bound > 0, err / bound, 0.0)
+    return float(r.max()) if r.size else 0.0

@@ -106,6 +106,54 @@ def test_scan_device_validation():
         assert big < (1 << 28) * eb // 100           # under 1% of the input bytes
 
 
+def test_scan_device_inclusive_validation():
+    L = sc.lib()
+    i32 = D["i32"]
+    need = L.scan_device_scratch_bytes(1000, i32)
+    assert L.scan_device_inclusive(A, B, 1000, i32, OP["mul"], S, need, None) == ENOTSUP
+    assert L.scan_device(A, B, 1000, i32, OP["mul"], S, need, None) == ENOTSUP
+    assert L.scan_device_inclusive(A, B, 1000, D["f16"], OP["add"], S, need, None) == ENOTSUP
+    assert L.scan_device_inclusive(A, B, 1000, i32, OP["add"], S, need - 1, None) == ESCRATCH
+    assert L.scan_device_inclusive(A, A + 3996, 1000, i32, OP["add"], S, need, None) == EALIAS
+    assert L.scan_device_inclusive(A, B, -3, i32, OP["add"], S, need, None) == EINVAL
+    assert L.scan_device_inclusive(A, B, 0, i32, OP["add"], None, 0, None) == OK
+
+
+def test_scan_rows_accepts_mul():
+    # validation passes for the product on every row dtype (empty shape: no launch)
+    for name in ("f32", "f16", "bf16"):
+        assert rows(A, B, 0, 16, D[name], OP["mul"], 0, None) == OK
+        assert rows(A, B, 4, 16, D[name], OP["mul"], 3, None) == EINVAL
+
+
+def test_reduce_validation():
+    L = sc.lib()
+    i32, f64 = D["i32"], D["f64"]
+    add = OP["add"]
+    need = L.reduce_device_scratch_bytes(1 << 20, i32)
+    assert need >= 16 and need % 16 == 0
+    assert L.reduce_device_scratch_bytes(0, i32) == 0
+    assert L.reduce_device_scratch_bytes(-1, i32) == 0
+    # at most one 8-byte partial per workgroup, and never more than 2048 of them
+    assert L.reduce_device_scratch_bytes(1 << 30, i32) <= 2048 * 8
+    assert L.reduce_device_scratch_bytes(1 << 30, f64) <= 2048 * 8
+    n = 1 << 20
+    assert L.reduce_device(A, B, n, D["bf16"], add, S, need, None) == ENOTSUP
+    assert L.reduce_device(A, B, n, i32, OP["mul"], S, need, None) == ENOTSUP
+    assert L.reduce_device(A, B, n, i32, 0, S, need, None) == ENOTSUP
+    assert L.reduce_device(A, B, -1, i32, add, S, need, None) == EINVAL
+    assert L.reduce_device(A, B, 1 << 31, i32, add, S, need, None) == EINVAL
+    assert L.reduce_device(A, None, n, i32, add, S, need, None) == EINVAL
+    assert L.reduce_device(A, B + 2, n, i32, add, S, need, None) == EINVAL     # out alignment
+    assert L.reduce_device(None, B, n, i32, add, S, need, None) == EINVAL
+    assert L.reduce_device(A, B, n, i32, add, None, need, None) == EINVAL
+    assert L.reduce_device(A, B, n, i32, add, S + 8, need, None) == EINVAL     # scratch alignment
+    assert L.reduce_device(A, B, n, i32, add, S, need - 16, None) == ESCRATCH
+    assert L.reduce_device(A, A + 4 * 100, n, i32, add, S, need, None) == EALIAS   # out in `in`
+    assert L.reduce_device(A, B, n, i32, add, A + 4096, need, None) == EALIAS      # scratch in `in`
+    assert L.reduce_device(A, S + 8, n, i32, add, S, need, None) == EALIAS         # out in scratch
+
+
 def test_select_validation():
     L = sc.lib()
     need = L.select_compact_scratch_bytes(1000)

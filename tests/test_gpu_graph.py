@@ -1,9 +1,9 @@
 """The library's calls captured into a HIP graph: every replay, with the
 program's own eager work and synchronizations in between, must reproduce the
-eager result bit for bit.  The three kernels are deterministic (row scans and
-integer / min-max device scans have a fixed combine order; select is exact),
-and each call resets its descriptors with a fill kernel rather than
-hipMemsetAsync, so it can sit in a graph."""
+eager result bit for bit.  Every kernel is deterministic (row scans, device
+scans and reductions have a fixed combine order for a given size and pointer
+alignment; select is exact), and each call resets its descriptors with a fill
+kernel rather than hipMemsetAsync, so it can sit in a graph."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,10 @@ def test_graph_replays_match_eager():
     y2 = torch.empty_like(xi)
     y3 = torch.empty_like(xf)
     y4 = torch.full_like(pay, -1.0)
+    y5 = torch.empty_like(xi)
+    y6 = torch.empty(1, dtype=torch.float32, device=dev)
+    y7 = torch.empty_like(x)
+    s6 = torch.empty(sc.reduce_device_scratch_bytes(nd, "f32"), dtype=torch.uint8, device=dev)
     num = torch.empty(1, dtype=torch.int32, device=dev)
     s2 = torch.empty(sc.scan_device_scratch_bytes(nd, "i32"), dtype=torch.uint8, device=dev)
     s3 = torch.empty(sc.scan_device_scratch_bytes(nd, "f32"), dtype=torch.uint8, device=dev)
@@ -46,6 +50,9 @@ def test_graph_replays_match_eager():
         sc.scan_device(xi, "add", out=y2, scratch=s2)
         sc.scan_device(xf, "max", out=y3, scratch=s3)
         sc.select_compact(pay, fl, out=y4, num_out=num, scratch=s4)
+        sc.scan_device_inclusive(xi, "add", out=y5, scratch=s2)
+        sc.reduce_device(xf, "add", out=y6, scratch=s6)
+        sc.scan_rows(x, "mul", False, out=y7)
 
     fill(0)
     side = torch.cuda.Stream()
@@ -62,12 +69,18 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (y1, y2, y3, y4, num)]
+        got = [t.clone() for t in (y1, y2, y3, y4, num, y5, y6, y7)]
         e1 = sc.scan_rows(x, "add", True)
         e2 = sc.scan_device(xi, "add")
         e3 = sc.scan_device(xf, "max")
         e4, en = sc.select_compact(pay, fl, out=torch.full_like(pay, -1.0))
+        e5 = sc.scan_device_inclusive(xi, "add")
+        e6 = sc.reduce_device(xf, "add")
+        e7 = sc.scan_rows(x, "mul", False)
         torch.cuda.synchronize()
+        assert torch.equal(got[5], e5), rep
+        assert torch.equal(got[6].view(torch.int32), e6.view(torch.int32)), rep
+        assert torch.equal(got[7].view(torch.int16), e7.view(torch.int16)), rep
         assert torch.equal(got[0].view(torch.int16), e1.view(torch.int16)), rep
         assert torch.equal(got[1], e2), rep
         assert torch.equal(got[2].view(torch.int32), e3.view(torch.int32)), rep

@@ -18,11 +18,17 @@ The five workloads (sizes, distributions and seeds):
    n = 2^27, and i64 uniform over the full range, seed 4, n = 2^26;
 5. select: f32 payload uniform [0, 1), seed 5, n = 2^28, and u8 flags
    Bernoulli(p), p in {0.01, 0.5, 0.99}, seed 6 + floor(100 p).
+
+Beyond the five: the product scans run on the row shapes of workloads 1 and 2
+with factors +-(1 + U[-1/64, 1/64)) (random sign), seed 11 for fp32 and 12
+for bf16, so that 8192-long products neither overflow nor underflow; the
+device-wide inclusive scans and the reductions reuse the inputs of workloads
+3 and 4 (plus an f32 add reduction of workload 4's f32 input).
 """
 import numpy as np
 
 SEEDS = {"rows_f32": 0, "rows_bf16": 1, "dev_i32": 2, "dev_f32": 3, "dev_i64": 4,
-         "sel_payload": 5}
+         "sel_payload": 5, "prod_f32": 11, "prod_bf16": 12}
 
 FULL = {
     "rows_f32": (1024, 4096),
@@ -85,6 +91,14 @@ def bernoulli_flags(n, p, seed):
     return (rng.random(size=n, dtype=np.float32) < np.float32(p)).astype(np.uint8)
 
 
+def near_one_f32(shape, seed):
+    """Factors +-(1 + U[-1/64, 1/64)) with a random sign, as float32."""
+    rng = np.random.default_rng(seed)
+    sign = rng.choice(np.array([-1.0, 1.0], np.float32), size=shape)
+    mag = rng.uniform(1 - 1 / 64, 1 + 1 / 64, size=shape).astype(np.float32)
+    return sign * mag
+
+
 def payload_f32(n, seed):
     rng = np.random.default_rng(seed)
     return rng.random(size=n, dtype=np.float32)
@@ -114,3 +128,11 @@ def dev_i64(n=FULL["dev_i64"], seed=SEEDS["dev_i64"]):
 
 def sel_inputs(n=FULL["sel"], p=0.5, seed=SEEDS["sel_payload"]):
     return payload_f32(n, seed), bernoulli_flags(n, p, flags_seed(p))
+
+
+def prod_rows_f32(rows=1024, n=4096, seed=SEEDS["prod_f32"]):
+    return near_one_f32((rows, n), seed)
+
+
+def prod_rows_bf16(rows=8192, n=8192, seed=SEEDS["prod_bf16"]):
+    return to_bf16_bits(near_one_f32((rows, n), seed))
