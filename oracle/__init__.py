@@ -21,6 +21,9 @@ computes, with the passages it follows:
 * ``reduce``: ``out[0] = op(x[0..n))`` per the "Algorithms" page, section
   ``qd.algorithms.reduce_{add,min,max}``: the final state of the same
   recurrence, the identity for an empty input.
+* ``reduce_by_key``: runs of equal consecutive keys collapsed into (first key,
+  sum of values) per the "Algorithms" page, section
+  ``qd.algorithms.reduce_by_key_add``.
 * ``select``: stream compaction per the "Algorithms" page, section
   ``qd.algorithms.select`` (stable, dense prefix, count).
 * ``f32_to_bf16`` / ``f32_to_f16`` and the widenings: round-to-nearest-even per
@@ -73,6 +76,8 @@ def lib():
         L.oracle_scan.restype = i32
         L.oracle_reduce.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         L.oracle_reduce.restype = i32
+        L.oracle_reduce_by_key.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_reduce_by_key.restype = i64
         L.oracle_select.argtypes = [vp, vp, vp, i64, i64]
         L.oracle_select.restype = i64
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -137,6 +142,33 @@ def reduce(x, dtype, op="add", want_ref=False):
     if want_ref:
         return out, float(ref[0]), float(absref[0])
     return out
+
+
+def reduce_by_key(keys, values, key_dtype, value_dtype, want_ref=False):
+    """Collapse runs of equal consecutive keys into (first key, sum of values).
+
+    ``keys`` / ``values`` hold the storage types of ``key_dtype`` /
+    ``value_dtype`` (each "i32", "u32" or "f32").  Returns ``(keys_out,
+    values_out, r)`` with ``len(keys)`` slots each (zero past ``r``); with
+    ``want_ref`` also per-run ``(ref, absref)`` float64 arrays (f32 values).
+    """
+    keys = np.ascontiguousarray(keys, dtype=STORAGE[key_dtype]).ravel()
+    values = np.ascontiguousarray(values, dtype=STORAGE[value_dtype]).ravel()
+    if keys.shape != values.shape:
+        raise ValueError("keys and values differ in length")
+    n = keys.shape[0]
+    ko = np.zeros(n, dtype=STORAGE[key_dtype])
+    vo = np.zeros(n, dtype=STORAGE[value_dtype])
+    ref = np.zeros(n, dtype=np.float64)
+    absref = np.zeros(n, dtype=np.float64)
+    r = lib().oracle_reduce_by_key(_ptr(keys), _ptr(values), n, DTYPES[key_dtype],
+                                   DTYPES[value_dtype], _ptr(ko), _ptr(vo), _ptr(ref),
+                                   _ptr(absref))
+    if r < 0:
+        raise ValueError("oracle_reduce_by_key rejected its arguments")
+    if want_ref:
+        return ko, vo, int(r), ref, absref
+    return ko, vo, int(r)
 
 
 def select(x, flags):

@@ -28,6 +28,16 @@
  *  - Stream compaction as defined on the "Algorithms" page, section
  *    qd.algorithms.select: every element whose flag is set is copied, in
  *    input order, into a dense prefix of out, and the count is returned.
+ *  - Reduce-by-key as defined on the "Algorithms" page, section
+ *    qd.algorithms.reduce_by_key_add: every maximal run of consecutive equal
+ *    keys becomes one output pair (key, sum of the run's values), in input
+ *    order, and the number of runs is returned.  Keys compare with the
+ *    key type's own ==, so a NaN key never equals anything (each NaN is a
+ *    run of its own) and +0 equals -0; the run's key is its first element's
+ *    key (the page's scatter leaves that choice to whichever write lands
+ *    last; the first is the deterministic reading).  Sums start from 0 and
+ *    fold the run in order: integer values wrap, f32 values accumulate in
+ *    double and are rounded once.
  *  - Reduction as defined on the "Algorithms" page, section
  *    qd.algorithms.reduce_{add,min,max}: out[0] = op over in[0..n), here
  *    the final state p[n] of the recurrence above (p[0], the identity, for
@@ -344,4 +354,70 @@ int64_t oracle_select(const void* in, const uint8_t* flags, void* out, int64_t n
         }
     }
     return k;
+}
+
+/* Reduce-by-key over n (key, value) pairs; keys and values are 32-bit (key
+ * dtype and value dtype each O_I32, O_U32 or O_F32).  Writes the runs'
+ * first keys to keys_out[0..r) and their value sums to values_out[0..r);
+ * nothing past r is written.  ref/absref (may be NULL) receive, per run, the
+ * double accumulator and the sum of |value| over the run.  Returns r, or -1
+ * for unsupported dtypes. */
+int64_t oracle_reduce_by_key(const void* keys, const void* values, int64_t n, int key_dtype,
+                             int value_dtype, void* keys_out, void* values_out, double* ref,
+                             double* absref) {
+    if (elem_size(key_dtype) != 4 || elem_size(value_dtype) != 4 || n < 0) return -1;
+    const uint32_t* kb = (const uint32_t*)keys;
+    const uint32_t* vb = (const uint32_t*)values;
+    uint32_t* ko = (uint32_t*)keys_out;
+    uint32_t* vo = (uint32_t*)values_out;
+    int64_t r = -1;                    /* index of the current run */
+    double dacc = 0.0, aacc = 0.0;     /* f32 values */
+    uint32_t iacc = 0u;                /* integer values, wrapping */
+    for (int64_t i = 0; i < n; ++i) {
+        int head;
+        if (i == 0) {
+            head = 1;
+        } else if (key_dtype == O_F32) {
+            float a, b;
+            memcpy(&a, &kb[i - 1], 4);
+            memcpy(&b, &kb[i], 4);
+            head = !(a == b);
+        } else {
+            head = kb[i] != kb[i - 1];
+        }
+        if (head) {
+            if (r >= 0) {              /* close the previous run */
+                if (value_dtype == O_F32) {
+                    float f = (float)dacc;
+                    memcpy(&vo[r], &f, 4);
+                    if (ref) ref[r] = dacc;
+                    if (absref) absref[r] = aacc;
+                } else {
+                    vo[r] = iacc;
+                }
+            }
+            ++r;
+            ko[r] = kb[i];
+            dacc = 0.0; aacc = 0.0; iacc = 0u;
+        }
+        if (value_dtype == O_F32) {
+            float f;
+            memcpy(&f, &vb[i], 4);
+            dacc += (double)f;
+            aacc += fabs((double)f);
+        } else {
+            iacc += vb[i];
+        }
+    }
+    if (r >= 0) {
+        if (value_dtype == O_F32) {
+            float f = (float)dacc;
+            memcpy(&vo[r], &f, 4);
+            if (ref) ref[r] = dacc;
+            if (absref) absref[r] = aacc;
+        } else {
+            vo[r] = iacc;
+        }
+    }
+    return r + 1;
 }

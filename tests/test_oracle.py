@@ -525,3 +525,90 @@ def test_reduce_minmax_signed_zero_takes_later(golden):
         red = oracle.reduce(x, "f32", case["op"])
         want = np.array([float(case["inclusive"][-1])], dtype=np.float32)
         assert red.view(np.uint32).tolist() == want.view(np.uint32).tolist(), case
+
+
+# ---- reduce-by-key -------------------------------------------------------------------------------
+
+def test_page_reduce_by_key_example(golden):
+    g = golden("reduce_by_key_example.json")
+    ko, vo, r = oracle.reduce_by_key(np.array(g["keys"], np.int32), np.array(g["values"], np.int32),
+                                     "i32", "i32")
+    assert r == g["num_runs"]
+    assert ko[:r].tolist() == g["keys_out"] and vo[:r].tolist() == g["values_out"]
+    assert not ko[r:].any() and not vo[r:].any()          # nothing written past the count
+
+
+def _groupby_runs(keys, values, key_is_float):
+    """Independent run split: a new run wherever the key differs from its predecessor."""
+    runs = []
+    for i, (k, v) in enumerate(zip(keys, values)):
+        same = i > 0 and ((keys[i - 1] == k) if not key_is_float else
+                          (float(keys[i - 1]) == float(k)))
+        if same:
+            runs[-1][1].append(v)
+        else:
+            runs.append((k, [v]))
+    return runs
+
+
+@pytest.mark.parametrize("kd", ["i32", "u32", "f32"])
+@pytest.mark.parametrize("vd", ["i32", "u32", "f32"])
+def test_reduce_by_key_brute_force(kd, vd):
+    rng = np.random.default_rng(100 * ["i32", "u32", "f32"].index(kd) + ["i32", "u32", "f32"].index(vd))
+    for n in (0, 1, 2, 3, 7, 50, 500):
+        keys = rng.integers(0, 3, size=n).astype(oracle.STORAGE[kd])    # short random runs
+        if vd == "f32":
+            values = rng.uniform(-2, 2, size=n).astype(np.float32)
+        else:
+            values = rng.integers(np.iinfo(oracle.STORAGE[vd]).min, np.iinfo(oracle.STORAGE[vd]).max,
+                                  size=n, endpoint=True).astype(oracle.STORAGE[vd])
+        ko, vo, r = oracle.reduce_by_key(keys, values, kd, vd)
+        runs = _groupby_runs(keys.tolist(), values.tolist(), kd == "f32")
+        assert r == len(runs), (kd, vd, n)
+        for j, (k, vs) in enumerate(runs):
+            assert ko[j] == k
+            if vd == "f32":
+                assert vo[j] == np.float32(math.fsum(vs)) or \
+                    abs(float(vo[j]) - math.fsum(vs)) <= 2 ** -24 * abs(math.fsum(vs)) + 1e-30
+            else:
+                w = sum(int(v) for v in vs) % (1 << 32)
+                assert int(np.array([vo[j]]).view(np.uint32)[0]) == w
+
+
+def test_reduce_by_key_invariants():
+    rng = np.random.default_rng(31)
+    n = 200_000
+    lengths = rng.geometric(1 / 8, size=n)
+    keys = np.repeat(rng.integers(0, 1 << 20, size=lengths.size), lengths)[:n].astype(np.int32)
+    values = rng.integers(-1000, 1000, size=n).astype(np.int32)
+    ko, vo, r = oracle.reduce_by_key(keys, values, "i32", "i32")
+    heads = np.flatnonzero(np.r_[True, keys[1:] != keys[:-1]])
+    assert r == heads.size
+    assert np.array_equal(ko[:r], keys[heads])                        # the runs' first keys
+    assert np.array_equal(vo[:r], np.add.reduceat(values, heads))     # numpy's segment sums
+    assert vo[:r].sum(dtype=np.int64) == values.sum(dtype=np.int64)
+
+
+def test_reduce_by_key_float_keys_nan_and_signed_zero():
+    nan = np.float32("nan")
+    keys = np.array([1.0, nan, nan, 0.0, -0.0, 0.0, 2.0, 2.0], np.float32)
+    values = np.array([1, 2, 3, 4, 5, 6, 7, 8], np.int32)
+    ko, vo, r = oracle.reduce_by_key(keys, values, "f32", "i32")
+    # each NaN is its own run; +0 and -0 compare equal, and the run keeps its first key (+0)
+    assert r == 5
+    assert vo[:r].tolist() == [1, 2, 3, 15, 15]
+    assert np.isnan(ko[1]) and np.isnan(ko[2])
+    assert ko[3] == 0.0 and math.copysign(1.0, float(ko[3])) == 1.0
+
+
+def test_reduce_by_key_f32_values_double_sum():
+    rng = np.random.default_rng(33)
+    keys = np.repeat(np.arange(50, dtype=np.int32), 1000)
+    values = rng.uniform(-1, 1, size=keys.size).astype(np.float32)
+    ko, vo, r, ref, absref = oracle.reduce_by_key(keys, values, "i32", "f32", want_ref=True)
+    assert r == 50
+    for j in range(r):
+        seg = values[j * 1000:(j + 1) * 1000].astype(np.float64)
+        exact = math.fsum(seg)
+        assert abs(ref[j] - exact) <= 1000 * 2.0 ** -53 * absref[j]
+        assert vo[j] == np.float32(ref[j])
