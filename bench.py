@@ -11,7 +11,7 @@ to nearest even).  Consecutive steps rotate over several input/output buffer
 pairs so that no step finds its data in the 256 MB Infinity Cache left there
 by the previous one.  The other workloads (row scans of fp32 [1024, 4096] and
 bf16 [8192, 8191], the bf16 product scan, the device-wide exclusive and
-inclusive scans, the reductions and select) are timed the same way and
+inclusive scans, the reductions, reduce-by-key and select) are timed the same way and
 reported inside the same JSON line under "workloads".
 
 Prints ONE JSON line.  "value" is elements/s of the headline workload (wall
@@ -39,6 +39,7 @@ KERNEL_SOURCES = {           # sources whose change invalidates stored counter r
     "scan_device": ["device.hpp", "scan_device.hip"],
     "select": ["device.hpp", "select.hip"],
     "reduce": ["device.hpp", "reduce.hip"],
+    "reduce_by_key": ["device.hpp", "reduce_by_key.hip"],
 }
 
 
@@ -318,6 +319,20 @@ def main():
         record(name, x5.numel(), x5.numel() * x5.element_size(), wall, per, K,
                "algorithmic bytes = n elements read; includes the one-wave final kernel")
         del x5, y5
+    if want("reduce_by_key"):
+        nk = wl.FULL["rbk"]
+        kk, vv = wl.rbk_inputs(nk)
+        kd, vd = torch.from_numpy(kk).to(dev), torch.from_numpy(vv).to(dev)
+        ko, vo = torch.empty_like(kd), torch.empty_like(vd)
+        nr = torch.empty(1, dtype=torch.int32, device=dev)
+        sk = torch.empty(sc.reduce_by_key_scratch_bytes(nk), dtype=torch.uint8, device=dev)
+        wall, per = timed(lambda i: sc.reduce_by_key(kd, vd, ko, vo, nr, sk), K, W)
+        runs = int(nr.item())
+        r = record("reduce_by_key", nk, nk * 8 + runs * 8 + 4, wall, per, K,
+                   "i32 keys in runs of mean length 8, f32 values; algorithmic bytes = 8n read "
+                   "+ 8 per run written + 4; includes the descriptor-reset fill kernel")
+        r["runs"] = runs
+        del kd, vd, ko, vo
     nsel = wl.FULL["sel"]
     for p in wl.SELECT_P:
         name = f"select_p{p}"

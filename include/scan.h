@@ -1,7 +1,8 @@
 /*
  * scan.h - C ABI of the stream_compaction_amd library (libscan_amd.so):
  * row-wise prefix scan, device-wide exclusive and inclusive scan, device-wide
- * reduction and stream compaction on one AMD Instinct MI355X (gfx950).
+ * reduction, reduce-by-key and stream compaction on one AMD Instinct MI355X
+ * (gfx950).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -147,6 +148,34 @@ scan_status scan_device_inclusive(const void* in, void* out, int64_t n, scan_dty
 size_t reduce_device_scratch_bytes(int64_t n, scan_dtype dtype);
 scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
                           void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Reduce-by-key ("Algorithms" page, section qd.algorithms.reduce_by_key_add):
+ * every maximal run of consecutive equal keys becomes one pair (the run's
+ * first key, the sum of its values), in input order; the number of runs r
+ * is written to num_runs[0] on the device.  keys_out[0..r) and
+ * values_out[0..r) receive the pairs; nothing past r is written.  Keys
+ * compare with their type's == (an f32 NaN key is a run of its own; +0 and
+ * -0 are equal).  Integer values wrap modulo 2^32; f32 sums are formed in
+ * float32 in a fixed regrouping of each run (deterministic for a given n and
+ * alignment), so their last bits may differ from a sequential sum.  One pass
+ * over the input (a segmented scan with decoupled look-back; no atomics).
+ *
+ *   keys_in      device pointer, n elements of key_dtype.
+ *   values_in    device pointer, n elements of value_dtype (may alias keys_in).
+ *   keys_out     device pointer, capacity n elements of key_dtype.
+ *   values_out   device pointer, capacity n elements of value_dtype.
+ *   num_runs     device pointer to one int32 (0 for n == 0).
+ *   key_dtype, value_dtype   each SCAN_I32, SCAN_U32 or SCAN_F32 (else
+ *                SCAN_ENOTSUP).
+ *   scratch      >= reduce_by_key_scratch_bytes(n) bytes, 16-byte aligned.
+ * Outputs, num_runs and scratch must not overlap each other or the inputs.
+ */
+size_t reduce_by_key_scratch_bytes(int64_t n);
+scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys_out,
+                          void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
+                          scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
+                          void* stream);
 
 /*
  * Stream compaction ("Algorithms" page, section qd.algorithms.select): every

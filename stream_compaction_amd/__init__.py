@@ -17,10 +17,12 @@ Entry points (same names as the C ABI):
   inclusive.
 * ``reduce_device(x, op="add", out=None, scratch=None)`` - device-wide
   reduction into a 1-element GPU tensor.
+* ``reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None,
+  scratch=None)`` - runs of equal consecutive keys collapsed into (key, sum).
 * ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
   stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
 * ``scan_device_scratch_bytes(n, dtype)``, ``reduce_device_scratch_bytes(n,
-  dtype)``, ``select_compact_scratch_bytes(n)``.
+  dtype)``, ``reduce_by_key_scratch_bytes(n)``, ``select_compact_scratch_bytes(n)``.
 """
 import ctypes
 import os
@@ -34,8 +36,9 @@ _STATUS = {0: "SCAN_OK", 1: "SCAN_EINVAL", 2: "SCAN_ENOTSUP", 3: "SCAN_EALIAS",
 DTYPE_CODES = {"f32": 1, "f16": 2, "bf16": 3, "f64": 4, "i32": 5, "u32": 6, "i64": 7, "u64": 8}
 OP_CODES = {"add": 1, "min": 2, "max": 3, "mul": 4}
 EXPORTS = ("scan_rows", "scan_device", "scan_device_inclusive", "scan_device_scratch_bytes",
-           "reduce_device", "reduce_device_scratch_bytes", "select_compact",
-           "select_compact_scratch_bytes", "scan_status_str", "scan_last_hip_error")
+           "reduce_device", "reduce_device_scratch_bytes", "reduce_by_key",
+           "reduce_by_key_scratch_bytes", "select_compact", "select_compact_scratch_bytes",
+           "scan_status_str", "scan_last_hip_error")
 
 _lib = None
 
@@ -71,6 +74,10 @@ def load(path):
     L.reduce_device_scratch_bytes.restype = sz
     L.reduce_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
     L.reduce_device.restype = i32
+    L.reduce_by_key_scratch_bytes.argtypes = [i64]
+    L.reduce_by_key_scratch_bytes.restype = sz
+    L.reduce_by_key.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, sz, vp]
+    L.reduce_by_key.restype = i32
     L.select_compact_scratch_bytes.argtypes = [i64]
     L.select_compact_scratch_bytes.restype = sz
     L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
@@ -212,6 +219,39 @@ def reduce_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
                               OP_CODES[op], _dev_ptr(scratch, "scratch"), scratch.numel(),
                               _stream(stream)))
     return out
+
+
+def reduce_by_key_scratch_bytes(n):
+    return int(lib().reduce_by_key_scratch_bytes(int(n)))
+
+
+def reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None, scratch=None,
+                  stream=None, key_dtype=None, value_dtype=None):
+    """Collapse runs of equal consecutive keys of the 1-D ``keys`` into (first key, sum of
+    ``values``).  Returns ``(keys_out, values_out, num_runs)``; ``num_runs`` is a 1-element
+    int32 GPU tensor and only the first ``num_runs`` entries of the outputs are written."""
+    torch = _torch()
+    if keys.dim() != 1 or values.dim() != 1 or keys.shape[0] != values.shape[0]:
+        raise ValueError("keys and values must be 1-D of the same length")
+    n = keys.shape[0]
+    kd, vd = _name(keys, key_dtype), _name(values, value_dtype)
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    if values_out is None:
+        values_out = torch.empty_like(values)
+    if keys_out.numel() < n or values_out.numel() < n or keys_out.dtype != keys.dtype or \
+            values_out.dtype != values.dtype:
+        raise ValueError("outputs must hold n elements of the inputs' dtypes")
+    if num_runs is None:
+        num_runs = torch.empty(1, dtype=torch.int32, device=keys.device)
+    need = reduce_by_key_scratch_bytes(n)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=keys.device)
+    check(lib().reduce_by_key(_dev_ptr(keys, "keys"), _dev_ptr(values, "values"),
+                              _dev_ptr(keys_out, "keys_out"), _dev_ptr(values_out, "values_out"),
+                              _dev_ptr(num_runs, "num_runs"), n, DTYPE_CODES[kd], DTYPE_CODES[vd],
+                              _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
+    return keys_out, values_out, num_runs
 
 
 def select_compact_scratch_bytes(n):

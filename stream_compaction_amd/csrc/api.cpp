@@ -159,6 +159,45 @@ scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype
   return hip_status(sca::launch_reduce(in, out, n, fmt, opi, scratch, (hipStream_t)stream));
 }
 
+size_t reduce_by_key_scratch_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return round16(sca::reduce_by_key_tiles(n) * 4 * 8);
+}
+
+scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys_out,
+                          void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
+                          scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
+                          void* stream) {
+  sca::Fmt kf, vf;
+  size_t keb, veb;
+  if (!fmt_of(key_dtype, &kf, &keb) || !fmt_of(value_dtype, &vf, &veb)) return SCAN_ENOTSUP;
+  auto ok32 = [](sca::Fmt f) {
+    return f == sca::Fmt::I32 || f == sca::Fmt::U32 || f == sca::Fmt::F32;
+  };
+  if (!ok32(kf) || !ok32(vf)) return SCAN_ENOTSUP;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
+  if (num_runs == nullptr || !aligned(num_runs, 4)) return SCAN_EINVAL;
+  if (n > 0) {
+    if (keys_in == nullptr || values_in == nullptr || keys_out == nullptr ||
+        values_out == nullptr || scratch == nullptr)
+      return SCAN_EINVAL;
+    if (!aligned(keys_in, 4) || !aligned(values_in, 4) || !aligned(keys_out, 4) ||
+        !aligned(values_out, 4) || !aligned(scratch, 16))
+      return SCAN_EINVAL;
+    const size_t need = reduce_by_key_scratch_bytes(n);
+    if (scratch_bytes < need) return SCAN_ESCRATCH;
+    const size_t bytes = (size_t)n * 4;
+    // the two inputs may share memory (both are only read); nothing else may
+    const void* r[6] = {keys_in, values_in, keys_out, values_out, num_runs, scratch};
+    const size_t z[6] = {bytes, bytes, bytes, bytes, 4, need};
+    for (int a = 0; a < 6; ++a)
+      for (int b = a + 1; b < 6; ++b)
+        if (!(a == 0 && b == 1) && overlap(r[a], z[a], r[b], z[b])) return SCAN_EALIAS;
+  }
+  return hip_status(sca::launch_reduce_by_key(keys_in, values_in, keys_out, values_out, num_runs,
+                                              n, kf, vf, scratch, (hipStream_t)stream));
+}
+
 size_t select_compact_scratch_bytes(int64_t n) {
   if (n < 0) return 0;
   return round16(sca::select_tiles(n, 8) * 8);

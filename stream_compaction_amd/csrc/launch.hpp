@@ -30,6 +30,13 @@ size_t reduce_partials(int64_t n, Fmt fmt);         // partials (8-byte slots) n
 hipError_t launch_reduce(const void* in, void* out, int64_t n, Fmt fmt, int op, void* scratch,
                          hipStream_t stream);
 
+// Reduce-by-key (32-bit keys and values): one descriptor (four 64-bit words)
+// per tile.
+size_t reduce_by_key_tiles(int64_t n);
+hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys_out,
+                                void* values_out, int32_t* num_runs, int64_t n, Fmt kfmt,
+                                Fmt vfmt, void* scratch, hipStream_t stream);
+
 // Stream compaction.
 size_t select_tiles(int64_t n, size_t elem_bytes);
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,

@@ -1,0 +1,323 @@
+// Reduce-by-key ("Algorithms" page, Quadrants user guide, section
+// qd.algorithms.reduce_by_key_add): every maximal run of consecutive equal
+// keys becomes one output pair (key, sum of the run's values), in input
+// order, and the number of runs goes to num_runs[0].
+//
+// The page realizes it as head flags, an exclusive scan of the flags into an
+// n-entry buffer, and a scatter that atomically adds every value into its run
+// (section "Under the hood").  Here one kernel does it in a single pass, with
+// no index buffer and no atomics, as a segmented scan ("Tile operations and
+// reductions": a segmented scan carries a lifted (head, value) state through
+// the same associative machinery):
+//   - element i carries the pair (h_i, v_i), h_i = 1 when it starts a run
+//     (i == 0 or key[i] differs from key[i-1]);
+//   - pairs combine as (c1, s1) (+) (c2, s2) = (c1 + c2, c2 ? s2 : s1 + s2):
+//     c counts the run starts in a span and s sums its values after the last
+//     start.  This is associative and keeps the earlier span on the left, so
+//     the DPP wave scan, the LDS exchange and the decoupled look-back of the
+//     device-wide scan carry it unchanged (tile descriptors hold the 64-bit
+//     pair);
+//   - with the exclusive pair (c, s) of a run-starting element i, run c
+//     begins at i: keys_out[c] = key[i]; and when c > 0, run c-1 ended at
+//     i-1 with sum s: values_out[c-1] = s.  The element at n-1 closes the
+//     last run and writes num_runs.
+// Keys compare with their own type's == (an f32 NaN key never equals
+// anything; +0 equals -0); each run keeps its first key.  Integer values
+// wrap modulo 2^32; f32 values are summed in float32 within a regrouping of
+// the run.  The input is read once; keys_out and values_out receive only the
+// runs (nothing past num_runs is written).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace sca {
+
+constexpr int64_t kRbkMinTileVecs = 512;
+
+// The scan state of a span: run starts in it and the sum after the last one.
+// V is float for f32 values and uint32_t for i32/u32 values (wrapping).
+template <class V>
+struct Seg {
+  uint32_t c;
+  V s;
+  Seg() = default;
+  __device__ __forceinline__ constexpr Seg(int) : c(0u), s(V(0)) {}   // the identity
+  __device__ __forceinline__ constexpr Seg(uint32_t c_, V s_) : c(c_), s(s_) {}
+};
+static_assert(sizeof(Seg<float>) == 8 && sizeof(Seg<uint32_t>) == 8, "one 64-bit word");
+
+// The segmented combine (a is the earlier span).  Found by argument-dependent
+// lookup from the generic wave scan and look-back, and preferred over the
+// generic combine as the more specialized template.
+template <Op O, class V>
+__device__ __forceinline__ Seg<V> combine(Seg<V> a, Seg<V> b) {
+  static_assert(O == Op::Add, "reduce-by-key sums");
+  const V s = b.c ? b.s : (V)(a.s + b.s);
+  return Seg<V>(a.c + b.c, s);
+}
+
+template <class KF> struct KeyEq;
+template <> struct KeyEq<FmtF32> {
+  static __device__ __forceinline__ bool eq(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(float, a) == __builtin_bit_cast(float, b);
+  }
+};
+template <> struct KeyEq<FmtI32> {
+  static __device__ __forceinline__ bool eq(uint32_t a, uint32_t b) { return a == b; }
+};
+template <> struct KeyEq<FmtU32> {
+  static __device__ __forceinline__ bool eq(uint32_t a, uint32_t b) { return a == b; }
+};
+
+template <class VF> struct ValT { using V = uint32_t; };
+template <> struct ValT<FmtF32> { using V = float; };
+
+template <int E>
+__device__ __forceinline__ uint32_t elem(const typename VecIO<uint32_t, E>::Raw& r, int k) {
+  if constexpr (E == 1) {
+    return r;
+  } else {
+    return k == 0 ? r.x : (k == 1 ? r.y : (k == 2 ? r.z : r.w));
+  }
+}
+
+// Key at window element i, or 0 bits (without touching memory) when i lies
+// outside [lo, hi).  Every lane reads the same word.
+__device__ __forceinline__ uint32_t key_at(uintptr_t k_base, int64_t i, int64_t lo, int64_t hi) {
+  const bool in = i >= lo && i < hi;
+  const Buf b(k_base + (in ? i : 0) * 4, in ? 4 : 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(b.r, 0, 0, 0);
+}
+
+template <class KF, class VF, int E, int WD, int K>
+__global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
+    uintptr_t k_base, uintptr_t v_base, int64_t n, int64_t ph, int64_t ntiles,
+    uintptr_t keys_out, uintptr_t values_out, uintptr_t num_runs, uint64_t* desc) {
+  using V = typename ValT<VF>::V;
+  using W = Seg<V>;
+  using IO = VecIO<uint32_t, E>;
+  using Raw = typename IO::Raw;
+  constexpr int64_t VB = (int64_t)E * 4;
+  constexpr int64_t kWaveVecs = (int64_t)kWave * K;
+  constexpr int64_t kTileVecs = kWaveVecs * WD;
+  static_assert(kTileVecs >= kRbkMinTileVecs, "scratch is sized for the smallest tile");
+  __shared__ W s_wave[WD];
+  __shared__ W s_prefix;
+  __shared__ uint32_t s_posted;
+
+  const int lane = lane_id(), wave = wave_id();
+  const int64_t tile = blockIdx.x;
+  const W id = W(0);
+  const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  if (threadIdx.x == 0) s_posted = 0u;
+  __syncthreads();
+
+  // K key and value vectors of the run of 64*K vectors starting at `first`.
+  auto load = [&](int64_t first, Raw (&rk)[K], Raw (&rv)[K]) {
+    const int64_t left = v_last + 1 - first;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf bk(k_base + first * VB, nv * VB), bv(v_base + first * VB, nv * VB);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      rk[j] = IO::load(bk, (uint32_t)((j * kWave + lane) * VB));
+      rv[j] = IO::load(bv, (uint32_t)((j * kWave + lane) * VB));
+    }
+  };
+  // Run-start bits (bit k: element k of the lane's vector) of load j, whose
+  // first vector is jv; `prev` is the key before the load's first element.
+  auto heads = [&](int64_t jv, const Raw& rk, uint32_t prev) -> uint32_t {
+    const uint32_t before = dpp<kWaveShr1, 0xf>(elem<E>(rk, E - 1), prev);
+    uint32_t h = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int64_t i = (jv + lane) * E + k;
+      const uint32_t p = k == 0 ? before : elem<E>(rk, k - 1);
+      const bool start = (i == lo) || !KeyEq<KF>::eq(elem<E>(rk, k), p);
+      h |= (i >= lo && i < hi && start) ? (1u << k) : 0u;
+    }
+    return h;
+  };
+  auto value = [&](const Raw& rv, int k, int64_t i) -> V {
+    return (i >= lo && i < hi) ? __builtin_bit_cast(V, elem<E>(rv, k)) : V(0);
+  };
+  // Lane total of load j (elements in order).
+  auto lane_total = [&](int64_t jv, const Raw& rv, uint32_t h) -> W {
+    W t = id;
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+      t = combine<Op::Add>(t, W((h >> k) & 1u, value(rv, k, (jv + lane) * E + k)));
+    return t;
+  };
+
+  if (wave < WD) {
+    // ---- data wave ----
+    const int64_t wb = tile * kTileVecs + wave * kWaveVecs;
+    Raw rk[K], rv[K];
+    load(wb, rk, rv);
+    uint32_t prev = key_at(k_base, wb * E - 1, lo, hi);
+    uint32_t hb[K];
+    W pre[K];
+    W carry = id;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t jv = wb + j * kWave;
+      hb[j] = heads(jv, rk[j], prev);
+      prev = readlane(elem<E>(rk[j], E - 1), kWave - 1);
+      const W incl = wave_scan_incl<Op::Add>(lane_total(jv, rv[j], hb[j]));
+      pre[j] = combine<Op::Add>(carry, wave_shift_excl<Op::Add>(incl));
+      carry = combine<Op::Add>(carry, readlane(incl, kWave - 1));
+    }
+    if (lane == 0) {
+      s_wave[wave] = carry;
+      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    W wp = s_prefix;
+    for (int w = 0; w < wave; ++w) wp = combine<Op::Add>(wp, s_wave[w]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t jv = wb + j * kWave;
+      W st = combine<Op::Add>(wp, pre[j]);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int64_t i = (jv + lane) * E + k;
+        const uint32_t h = (hb[j] >> k) & 1u;
+        // (run indices never reach n; the bound only keeps every store
+        // inside the caller's n-element outputs whatever the input)
+        if (h && st.c < (uint64_t)n) {
+          *gptr<uint32_t>(keys_out + (uintptr_t)st.c * 4) = elem<E>(rk[j], k);
+          if (st.c > 0) *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+        }
+        st = combine<Op::Add>(st, W(h, value(rv[j], k, i)));
+        // the last element closes the last run
+        if (i == hi - 1 && st.c >= 1 && st.c <= (uint64_t)n) {
+          *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+          *gptr<int32_t>(num_runs) = (int32_t)st.c;
+        }
+      }
+    }
+  } else {
+    // ---- look-back wave ----
+    auto posted = [&]() {
+      return __hip_atomic_load(&s_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+             (uint32_t)WD;
+    };
+    auto tile_agg = [&]() {
+      W a = s_wave[0];
+#pragma unroll
+      for (int w = 1; w < WD; ++w) a = combine<Op::Add>(a, s_wave[w]);
+      return a;
+    };
+    W prefix = id;
+    if (tile > 0) {
+      bool agg_published = false;
+      auto idle = [&]() {
+        if (!agg_published && posted()) {
+          if (lane == 0) Desc<W>::publish(desc, tile, kAgg, tile_agg());
+          agg_published = true;
+        }
+      };
+      // fallback for a late predecessor: fold its input in element order
+      auto reduce_tile = [&](int64_t t) -> W {
+        W acc = id;
+        uint32_t prev = key_at(k_base, t * kTileVecs * E - 1, lo, hi);
+        for (int c = 0; c < WD; ++c) {
+          Raw rk[K], rv[K];
+          const int64_t first = t * kTileVecs + c * kWaveVecs;
+          load(first, rk, rv);
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            const int64_t jv = first + j * kWave;
+            const uint32_t h = heads(jv, rk[j], prev);
+            prev = readlane(elem<E>(rk[j], E - 1), kWave - 1);
+            acc = combine<Op::Add>(
+                acc, readlane(wave_scan_incl<Op::Add>(lane_total(jv, rv[j], h)), kWave - 1));
+          }
+        }
+        return acc;
+      };
+      prefix = look_back<Op::Add, W>(desc, tile, kLookBackTimeout, reduce_tile, idle);
+    }
+    while (!posted()) __builtin_amdgcn_s_sleep(1);
+    if (lane == 0) {
+      Desc<W>::publish(desc, tile, kInc, combine<Op::Add>(prefix, tile_agg()));
+      s_prefix = prefix;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void rbk_count_zero_kernel(int32_t* num_runs) { *num_runs = 0; }
+
+static int64_t rbk_tiles_for(int64_t n, int e, int64_t tv) {
+  if (n <= 0) return 0;
+  const int64_t v_last = (n - 1 + (e - 1)) / e;
+  return v_last / tv + 1;
+}
+
+// Sized for the one-element-per-vector path and the smallest tile.
+size_t reduce_by_key_tiles(int64_t n) { return (size_t)rbk_tiles_for(n, 1, kRbkMinTileVecs); }
+
+template <class KF, class VF, int WD, int K>
+static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* keys_out,
+                                 void* values_out, int32_t* num_runs, int64_t n, void* scratch,
+                                 hipStream_t stream) {
+  constexpr int64_t TV = (int64_t)kWave * WD * K;
+  const uintptr_t ka = (uintptr_t)keys, va = (uintptr_t)values;
+  const bool vec = (ka % 16) == (va % 16);
+  const int e = vec ? 4 : 1;
+  const int64_t ph = vec ? (int64_t)((ka % 16) / 4) : 0;
+  const int64_t ntiles = rbk_tiles_for(n, e, TV);
+  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * 4 * 8, stream);
+  if (err != hipSuccess) return err;
+  const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
+  const uintptr_t ko = (uintptr_t)keys_out, vo = (uintptr_t)values_out, nr = (uintptr_t)num_runs;
+  if (vec) {
+    reduce_by_key_kernel<KF, VF, 4, WD, K><<<grid, block, 0, stream>>>(
+        ka - ph * 4, va - ph * 4, n, ph, ntiles, ko, vo, nr, (uint64_t*)scratch);
+  } else {
+    reduce_by_key_kernel<KF, VF, 1, WD, K><<<grid, block, 0, stream>>>(
+        ka, va, n, 0, ntiles, ko, vo, nr, (uint64_t*)scratch);
+  }
+  return hipGetLastError();
+}
+
+template <class KF, class VF>
+static hipError_t launch_rbk_t(const void* keys, const void* values, void* keys_out,
+                               void* values_out, int32_t* num_runs, int64_t n, void* scratch,
+                               hipStream_t stream) {
+  return launch_rbk_cfg<KF, VF, 7, 8>(keys, values, keys_out, values_out, num_runs, n, scratch,
+                                      stream);
+}
+
+template <class KF>
+static hipError_t launch_rbk_k(const void* keys, const void* values, void* keys_out,
+                               void* values_out, int32_t* num_runs, int64_t n, Fmt vfmt,
+                               void* scratch, hipStream_t stream) {
+  switch (vfmt) {
+    case Fmt::F32:
+      return launch_rbk_t<KF, FmtF32>(keys, values, keys_out, values_out, num_runs, n, scratch,
+                                      stream);
+    default:   // i32 and u32 values share the wrapping add
+      return launch_rbk_t<KF, FmtU32>(keys, values, keys_out, values_out, num_runs, n, scratch,
+                                      stream);
+  }
+}
+
+hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys_out,
+                                void* values_out, int32_t* num_runs, int64_t n, Fmt kfmt,
+                                Fmt vfmt, void* scratch, hipStream_t stream) {
+  if (n == 0) {
+    rbk_count_zero_kernel<<<dim3(1), dim3(1), 0, stream>>>(num_runs);
+    return hipGetLastError();
+  }
+  switch (kfmt) {
+    case Fmt::F32:
+      return launch_rbk_k<FmtF32>(keys, values, keys_out, values_out, num_runs, n, vfmt, scratch,
+                                  stream);
+    default:   // i32 and u32 keys compare as bits
+      return launch_rbk_k<FmtU32>(keys, values, keys_out, values_out, num_runs, n, vfmt, scratch,
+                                  stream);
+  }
+}
+
+}  // namespace sca

@@ -180,3 +180,33 @@ def test_binding_maps_status_to_exceptions():
     with pytest.raises(sc.ScanError):
         sc.check(5)
     sc.check(OK)
+
+
+def test_reduce_by_key_validation():
+    L = sc.lib()
+    n = 1000
+    need = L.reduce_by_key_scratch_bytes(n)
+    assert need >= 32 and need % 16 == 0
+    assert L.reduce_by_key_scratch_bytes(-1) == 0
+    i32, f32 = D["i32"], D["f32"]
+    K, V, KO, VO, NR = A, A + 0x10000, B, B + 0x10000, B + 0x20000
+
+    def call(*, k=K, v=V, ko=KO, vo=VO, nr=NR, nn=n, kd=i32, vd=f32, s=S, sb=need):
+        return L.reduce_by_key(k, v, ko, vo, nr, nn, kd, vd, s, sb, None)
+    assert call(kd=D["i64"]) == ENOTSUP
+    assert call(vd=D["f64"]) == ENOTSUP
+    assert call(kd=D["bf16"]) == ENOTSUP
+    assert call(nn=-1) == EINVAL
+    assert call(nn=1 << 31) == EINVAL
+    assert call(nr=None) == EINVAL
+    assert call(nr=NR + 2) == EINVAL
+    assert call(k=None) == EINVAL
+    assert call(vo=VO + 2) == EINVAL
+    assert call(s=S + 8) == EINVAL
+    assert call(sb=need - 16) == ESCRATCH
+    assert call(ko=K + 400) == EALIAS                 # keys_out over keys_in
+    assert call(vo=KO + 400) == EALIAS                # the two outputs overlap
+    assert call(nr=VO + 40) == EALIAS                 # num_runs inside values_out
+    assert call(s=V + 64) == EALIAS                   # scratch inside values_in
+    # (calls that pass validation would launch on these fake addresses, so the
+    # accepted cases, aliased inputs and n == 0 included, run in the GPU tests)

@@ -305,3 +305,141 @@ def test_lookback_recovery_build_inclusive():
                                          sc.OP_CODES[op], scratch.data_ptr(), need, stream))
         torch.cuda.synchronize()
         compare_incl(from_dev(yd, dt), x, dt, op, f"fallback build inclusive {dt} {op} n={n}")
+
+
+# ---------------------------------------------------------------------------
+# reduce-by-key
+# ---------------------------------------------------------------------------
+
+def run_lengths_keys(n, mean_run, seed, dt="i32"):
+    """Keys in runs of geometric length (mean `mean_run`), each run a random key."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.geometric(1.0 / mean_run, size=n // max(1, int(mean_run)) + 16)
+    while lengths.sum() < n:
+        lengths = np.r_[lengths, rng.geometric(1.0 / mean_run, size=lengths.size)]
+    keys = np.repeat(rng.integers(0, 8, size=lengths.size), lengths)[:n]
+    if dt == "f32":
+        return keys.astype(np.float32)
+    return keys.astype(oracle.STORAGE[dt])
+
+
+def rbk_values(n, vd, seed):
+    rng = np.random.default_rng(seed)
+    if vd == "f32":
+        return rng.uniform(-1, 1, size=n).astype(np.float32)
+    info = np.iinfo(oracle.STORAGE[vd])
+    return rng.integers(info.min, info.max, size=n, endpoint=True).astype(oracle.STORAGE[vd])
+
+
+def check_rbk(keys, values, kd, vd, label, key_out=None, val_out=None):
+    n = keys.size
+    kdev, vdev = to_dev(keys, kd), to_dev(values, vd)
+    ko = to_dev(np.full(n, 0x5A5A5A5A, np.uint32).view(oracle.STORAGE[kd]), kd) \
+        if key_out is None else key_out
+    vo = to_dev(np.full(n, 0x5A5A5A5A, np.uint32).view(oracle.STORAGE[vd]), vd) \
+        if val_out is None else val_out
+    _, _, nr = sc.reduce_by_key(kdev, vdev, ko, vo, key_dtype=kd, value_dtype=vd)
+    r = int(nr.item())
+    oko, ovo, orr, ref, absref = oracle.reduce_by_key(keys, values, kd, vd, want_ref=True)
+    assert r == orr, f"{label}: {r} runs, oracle {orr}"
+    gk, gv = from_dev(ko, kd), from_dev(vo, vd)
+    check_exact(gk[:r], oko[:r], label + " keys")
+    if vd == "f32":
+        bound = FP_REL * absref[:r] + FP_ABS
+        err = np.abs(gv[:r].astype(np.float64) - ref[:r])
+        assert (err <= bound).all(), f"{label}: value out of tolerance at run {np.argmax(err > bound)}"
+    else:
+        check_exact(gv[:r], ovo[:r], label + " values")
+    assert (gk[r:].view(np.uint32) == 0x5A5A5A5A).all(), f"{label}: keys tail written"
+    assert (gv[r:].view(np.uint32) == 0x5A5A5A5A).all(), f"{label}: values tail written"
+    return r
+
+
+RBK_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 28671, 28672,
+             28673, 100_003, 1_000_003, 3_000_017]
+
+
+@pytest.mark.parametrize("kd,vd", [("i32", "i32"), ("i32", "f32"), ("u32", "u32"),
+                                   ("f32", "f32"), ("f32", "i32")])
+@pytest.mark.parametrize("mean_run", [1, 3, 40])
+def test_reduce_by_key_sizes(kd, vd, mean_run):
+    for i, n in enumerate(RBK_SIZES):
+        keys = run_lengths_keys(n, mean_run, 9000 + i, kd)
+        values = rbk_values(n, vd, 9100 + i)
+        check_rbk(keys, values, kd, vd, f"reduce_by_key {kd}/{vd} mean run {mean_run} n={n}")
+
+
+def test_reduce_by_key_single_run_and_all_unique():
+    n = 2_000_003
+    check_rbk(np.zeros(n, np.int32), rbk_values(n, "i32", 1), "i32", "i32", "one run")
+    check_rbk(np.arange(n, dtype=np.int32), rbk_values(n, "i32", 2), "i32", "i32", "all unique")
+
+
+def test_reduce_by_key_float_keys_nan_and_zeros():
+    rng = np.random.default_rng(12)
+    vals = np.array([np.nan, 0.0, -0.0, 1.0, -1.0], np.float32)
+    keys = vals[rng.integers(0, len(vals), size=300_001)]
+    check_rbk(keys, rbk_values(keys.size, "i32", 3), "f32", "i32", "nan and signed-zero keys")
+
+
+def test_reduce_by_key_misaligned_and_aliased():
+    n = 200_003
+    keys = run_lengths_keys(n, 5, 77)
+    values = rbk_values(n, "i32", 78)
+    for off_k, off_v in ((1, 1), (0, 3), (2, 1)):
+        bk = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
+        bv = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
+        kin, vin = bk[off_k:off_k + n], bv[off_v:off_v + n]
+        kin.copy_(torch.from_numpy(keys).cuda())
+        vin.copy_(torch.from_numpy(values).cuda())
+        ko, vo, nr = sc.reduce_by_key(kin, vin)
+        r = int(nr.item())
+        oko, ovo, orr = oracle.reduce_by_key(keys, values, "i32", "i32")
+        assert r == orr
+        check_exact(ko.cpu().numpy()[:r], oko[:r], f"misaligned keys {off_k},{off_v}")
+        check_exact(vo.cpu().numpy()[:r], ovo[:r], f"misaligned values {off_k},{off_v}")
+    # keys and values the same array: a run's value is its key times its length
+    kd = to_dev(keys, "i32")
+    ko, vo, nr = sc.reduce_by_key(kd, kd)
+    r = int(nr.item())
+    oko, ovo, orr = oracle.reduce_by_key(keys, keys, "i32", "i32")
+    assert r == orr
+    check_exact(vo.cpu().numpy()[:r], ovo[:r], "aliased inputs")
+
+
+def test_reduce_by_key_empty():
+    k = torch.zeros(0, dtype=torch.int32, device="cuda")
+    nr = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+    sc.reduce_by_key(k, k.clone(), num_runs=nr)
+    assert int(nr.item()) == 0
+
+
+def test_reduce_by_key_full():
+    n = workloads.FULL["rbk"]
+    keys, values = workloads.rbk_inputs(n)
+    label = f"reduce_by_key i32/f32 n={n} mean run {workloads.RBK_MEAN_RUN}"
+    note(label)
+    r = check_rbk(keys, values, "i32", "f32", label)
+    note(f"  runs {r}")
+
+
+def test_lookback_recovery_build_reduce_by_key():
+    from stream_compaction_amd import build as b
+    L = sc.load(b.FALLBACK_LIB_PATH)
+    stream = torch.cuda.current_stream().cuda_stream
+    n = 2_000_003
+    keys = run_lengths_keys(n, 6, 321)
+    values = rbk_values(n, "i32", 322)
+    kd, vd = to_dev(keys, "i32"), to_dev(values, "i32")
+    ko, vo = torch.empty_like(kd), torch.empty_like(vd)
+    nr = torch.empty(1, dtype=torch.int32, device="cuda")
+    need = L.reduce_by_key_scratch_bytes(n)
+    scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+    sc.check(L.reduce_by_key(kd.data_ptr(), vd.data_ptr(), ko.data_ptr(), vo.data_ptr(),
+                             nr.data_ptr(), n, sc.DTYPE_CODES["i32"], sc.DTYPE_CODES["i32"],
+                             scratch.data_ptr(), need, stream))
+    r = int(nr.item())
+    oko, ovo, orr = oracle.reduce_by_key(keys, values, "i32", "i32")
+    assert r == orr
+    check_exact(ko.cpu().numpy()[:r], oko[:r], "fallback build keys")
+    check_exact(vo.cpu().numpy()[:r], ovo[:r], "fallback build values")

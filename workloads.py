@@ -23,12 +23,14 @@ Beyond the five: the product scans run on the row shapes of workloads 1 and 2
 with factors +-(1 + U[-1/64, 1/64)) (random sign), seed 11 for fp32 and 12
 for bf16, so that 8192-long products neither overflow nor underflow; the
 device-wide inclusive scans and the reductions reuse the inputs of workloads
-3 and 4 (plus an f32 add reduction of workload 4's f32 input).
+3 and 4 (plus an f32 add reduction of workload 4's f32 input); reduce-by-key
+runs on n = 2^27 i32 keys in runs of geometric length with mean 8 (each run's
+key uniform in [0, 2^20), seed 13) and f32 values uniform [0, 1) (seed 14).
 """
 import numpy as np
 
 SEEDS = {"rows_f32": 0, "rows_bf16": 1, "dev_i32": 2, "dev_f32": 3, "dev_i64": 4,
-         "sel_payload": 5, "prod_f32": 11, "prod_bf16": 12}
+         "sel_payload": 5, "prod_f32": 11, "prod_bf16": 12, "rbk_keys": 13, "rbk_values": 14}
 
 FULL = {
     "rows_f32": (1024, 4096),
@@ -39,7 +41,9 @@ FULL = {
     "dev_f32": 1 << 27,
     "dev_i64": 1 << 26,
     "sel": 1 << 28,
+    "rbk": 1 << 27,
 }
+RBK_MEAN_RUN = 8
 SELECT_P = (0.01, 0.5, 0.99)
 
 
@@ -136,3 +140,18 @@ def prod_rows_f32(rows=1024, n=4096, seed=SEEDS["prod_f32"]):
 
 def prod_rows_bf16(rows=8192, n=8192, seed=SEEDS["prod_bf16"]):
     return to_bf16_bits(near_one_f32((rows, n), seed))
+
+
+def run_keys(n, mean_run, seed, key_range=1 << 20):
+    """n int32 keys in runs of geometric length (mean `mean_run`), each run's key
+    uniform in [0, key_range)."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.geometric(1.0 / mean_run, size=int(n / mean_run * 1.1) + 64)
+    while lengths.sum() < n:
+        lengths = np.concatenate([lengths, rng.geometric(1.0 / mean_run, size=lengths.size)])
+    return np.repeat(rng.integers(0, key_range, size=lengths.size).astype(np.int32), lengths)[:n]
+
+
+def rbk_inputs(n=FULL["rbk"]):
+    keys = run_keys(n, RBK_MEAN_RUN, SEEDS["rbk_keys"])
+    return keys, payload_f32(n, SEEDS["rbk_values"])
