@@ -388,14 +388,15 @@ template <class W> struct Desc<W, 8> {
     st_relaxed(slot, (1ull << 32) | (uint32_t)u);
     st_relaxed(slot + 1, (1ull << 32) | (uint32_t)(u >> 32));
   }
+  // All four words are loaded together (one round trip, not two).
   static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
     const uint64_t* s = d + tile * 4;
+    const uint64_t alo = ld_relaxed(s), ahi = ld_relaxed(s + 1);
     const uint64_t ilo = ld_relaxed(s + 2), ihi = ld_relaxed(s + 3);
     if ((ilo >> 32) && (ihi >> 32)) {
       v = __builtin_bit_cast(W, (ihi << 32) | (uint32_t)ilo);
       return kInc;
     }
-    const uint64_t alo = ld_relaxed(s), ahi = ld_relaxed(s + 1);
     if ((alo >> 32) && (ahi >> 32)) {
       v = __builtin_bit_cast(W, (ahi << 32) | (uint32_t)alo);
       return kAgg;
@@ -403,6 +404,37 @@ template <class W> struct Desc<W, 8> {
     return kNone;
   }
 };
+
+// A data wave's part in publishing its tile's aggregate (called by lane 0 of
+// each of the WD data waves, once): the wave posts its total to s_wave and
+// counts itself in *s_posted; the last of the WD waves to do so combines the
+// totals in wave order, publishes the tile's aggregate descriptor at once
+// (tile 0 publishes its inclusive prefix instead, later) and raises
+// *s_agg_done, after which the look-back wave may read s_wave and publish
+// the inclusive prefix.  Publishing from the data side, rather than from the
+// look-back wave between two of its polls, lets successors see the aggregate
+// as soon as it exists; and because the inclusive prefix is only published
+// after *s_agg_done, it can never be overwritten by the aggregate.
+template <Op O, class W, int WD>
+__device__ __forceinline__ void post_wave_total(W total, int wave, int64_t tile, W* s_wave,
+                                                uint32_t* s_posted, uint32_t* s_agg_done,
+                                                uint64_t* desc) {
+  s_wave[wave] = total;
+  const uint32_t before =
+      __hip_atomic_fetch_add(s_posted, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (before == (uint32_t)WD - 1) {
+    W a = s_wave[0];
+#pragma unroll
+    for (int w = 1; w < WD; ++w) a = combine<O>(a, s_wave[w]);
+    if (tile > 0) Desc<W>::publish(desc, tile, kAgg, a);
+    __hip_atomic_store(s_agg_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+__device__ __forceinline__ bool lds_flag_set(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_ACQUIRE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP) != 0u;
+}
 
 // Look-back by one wave: returns the combine of every tile before `tile`
 // (the tile's exclusive prefix).  Lane l inspects tile base - 63 + l, so lane
@@ -420,18 +452,27 @@ template <class W> struct Desc<W, 8> {
 // changes, so this is exactly what that tile would publish).  The walk then
 // needs nothing from workgroups that have not started, so it ends whatever
 // order the hardware runs workgroups in; in the usual case no descriptor is
-// that late and no tile is reduced twice.  idle() runs between polls (the
-// caller publishes its own aggregate there as soon as it is known).
-// Pause between descriptor polls: s_sleep 127 (about 8k cycles, ~3.4 us).
-// Polling is not free on MI355X: every poll is a device-scope read that goes
-// past the XCD's L2, and with a thousand tiles waiting at once short pauses
-// measurably slowed the data traffic (2^28 i32 scan: 517 us at s_sleep 1,
-// 443 us at 100, 436 us at 127).
-constexpr int kPollSleep = 127;
+// that late and no tile is reduced twice.
+// Pauses between descriptor polls, in s_sleep units of 64 cycles (127: about
+// 8k cycles, ~3.4 us).  Polling is not free on MI355X: every poll is a
+// device-scope read that goes past the XCD's L2, and with hundreds of tiles
+// waiting at once short pauses between window polls measurably slow the data
+// traffic (2^28 i32 scan: 419 us with a window pause of 16, 410 us at 32,
+// 385 us at 127).  The pre-wait polls one descriptor, and its pause length
+// made no measurable difference (2: 388 us, 127: 385 us).  Both can be
+// overridden at compile time for measurements.
+#ifndef SCA_PREWAIT_SLEEP
+#define SCA_PREWAIT_SLEEP 127
+#endif
+#ifndef SCA_WINDOW_SLEEP
+#define SCA_WINDOW_SLEEP 127
+#endif
+constexpr int kPreWaitSleep = SCA_PREWAIT_SLEEP;
+constexpr int kPollSleep = SCA_WINDOW_SLEEP;
 
-template <Op O, class W, class ReduceTile, class Idle>
+template <Op O, class W, class ReduceTile>
 __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint64_t timeout,
-                                       ReduceTile&& reduce_tile, Idle&& idle) {
+                                       ReduceTile&& reduce_tile) {
   const int lane = lane_id();
   const W id = identity<O, W>();
   W prefix = id;
@@ -443,8 +484,7 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
     W v;
     while (Desc<W>::read(desc, tile - 1, v) == kNone &&
            __builtin_amdgcn_s_memrealtime() - t0 <= timeout) {
-      idle();
-      __builtin_amdgcn_s_sleep(kPollSleep);
+      __builtin_amdgcn_s_sleep(kPreWaitSleep);
     }
   }
   for (int64_t base = tile - 1;; base -= kWave) {
@@ -472,7 +512,6 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
         }
         break;
       }
-      idle();
       __builtin_amdgcn_s_sleep(kPollSleep);
     }
     const uint64_t inc = __ballot(st == kInc);

@@ -103,12 +103,16 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
   __shared__ W s_wave[WD];
   __shared__ W s_prefix;
   __shared__ uint32_t s_posted;
+  __shared__ uint32_t s_agg_done;
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const W id = W(0);
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
-  if (threadIdx.x == 0) s_posted = 0u;
+  if (threadIdx.x == 0) {
+    s_posted = 0u;
+    s_agg_done = 0u;
+  }
   __syncthreads();
 
   // K key and value vectors of the run of 64*K vectors starting at `first`.
@@ -167,8 +171,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
       carry = combine<Op::Add>(carry, readlane(incl, kWave - 1));
     }
     if (lane == 0) {
-      s_wave[wave] = carry;
-      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      post_wave_total<Op::Add, W, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done, desc);
     }
     __syncthreads();
     W wp = s_prefix;
@@ -197,10 +200,6 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     }
   } else {
     // ---- look-back wave ----
-    auto posted = [&]() {
-      return __hip_atomic_load(&s_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
-             (uint32_t)WD;
-    };
     auto tile_agg = [&]() {
       W a = s_wave[0];
 #pragma unroll
@@ -209,13 +208,6 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     };
     W prefix = id;
     if (tile > 0) {
-      bool agg_published = false;
-      auto idle = [&]() {
-        if (!agg_published && posted()) {
-          if (lane == 0) Desc<W>::publish(desc, tile, kAgg, tile_agg());
-          agg_published = true;
-        }
-      };
       // fallback for a late predecessor: fold its input in element order
       auto reduce_tile = [&](int64_t t) -> W {
         W acc = id;
@@ -235,9 +227,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
         }
         return acc;
       };
-      prefix = look_back<Op::Add, W>(desc, tile, kLookBackTimeout, reduce_tile, idle);
+      prefix = look_back<Op::Add, W>(desc, tile, kLookBackTimeout, reduce_tile);
     }
-    while (!posted()) __builtin_amdgcn_s_sleep(1);
+    while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
       Desc<W>::publish(desc, tile, kInc, combine<Op::Add>(prefix, tile_agg()));
       s_prefix = prefix;

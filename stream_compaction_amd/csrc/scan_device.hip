@@ -10,22 +10,22 @@
 //  - Each data wave loads its run of 64*K 16-byte vectors (load j of lane l
 //    is vector j*64 + l of the run, so every load instruction covers 1 KiB),
 //    scans every vector lane-serially and the 64 lane totals with a DPP wave
-//    scan, and posts its wave total to LDS.
+//    scan, and posts its wave total to LDS; the last data wave to post
+//    publishes the tile's aggregate at once.
 //  - The look-back wave starts walking back over the predecessors'
 //    descriptors as soon as the workgroup starts, while the data is still in
-//    flight: the walk needs nothing from this tile.  Between polls it
-//    publishes the tile's aggregate once all wave totals are posted; when the
-//    walk ends it publishes the tile's inclusive prefix and hands the
-//    exclusive prefix to the data waves through LDS.
+//    flight: the walk needs nothing from this tile.  When the walk ends and
+//    the aggregate is out, it publishes the tile's inclusive prefix and hands
+//    the exclusive prefix to the data waves through LDS.
 //  - The data waves then combine tile prefix, earlier waves, earlier vectors
 //    and earlier elements of the vector, and store.
 // The input is read once and the output written once.  Tile ids are the
 // workgroup ids: no atomic counter (a device-wide atomic on one address
 // serializes at about 11 ns per tile on MI355X); the look-back's bounded wait
 // (device.hpp) keeps this correct and deadlock-free under any workgroup order.
-// The look-back wave learns that the wave totals are posted from an LDS
-// counter (no barrier), so it never holds up the data waves' loads and scans;
-// one barrier then hands the prefix back, with the data waves asleep in it.
+// The waves meet through an LDS counter and flag (no barrier), so the
+// look-back never holds up the data waves' loads and scans; one barrier then
+// hands the prefix back, with the data waves asleep in it.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -33,10 +33,6 @@ namespace sca {
 
 // Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
 constexpr int64_t kDevMinTileVecs = 512;
-
-__device__ __forceinline__ uint32_t lds_acquire(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 
 template <class F, Op O, bool INCL, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
@@ -51,12 +47,16 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
   __shared__ W s_wave[WD];
   __shared__ W s_prefix;
   __shared__ uint32_t s_posted;   // data waves whose totals are in s_wave
+  __shared__ uint32_t s_agg_done; // the tile's aggregate is published
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const W id = identity<O, W>();
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
-  if (threadIdx.x == 0) s_posted = 0u;
+  if (threadIdx.x == 0) {
+    s_posted = 0u;
+    s_agg_done = 0u;
+  }
   __syncthreads();
 
   // A wave's K loads of the run of 64*K vectors starting at `first` (zero bits past v_last).
@@ -93,10 +93,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
       pre[j] = combine<O>(carry, wave_shift_excl<O>(incl));
       carry = combine<O>(carry, readlane(incl, kWave - 1));
     }
-    if (lane == 0) {
-      s_wave[wave] = carry;
-      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    if (lane == 0) post_wave_total<O, W, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done, desc);
     __syncthreads();  // sleeps in hardware until the look-back wave has the prefix
     W wp = s_prefix;
     for (int w = 0; w < wave; ++w) wp = combine<O>(wp, s_wave[w]);
@@ -117,7 +114,6 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     }
   } else {
     // ---- look-back wave ----
-    auto posted = [&]() { return lds_acquire(&s_posted) == (uint32_t)WD; };
     auto tile_agg = [&]() {
       W a = s_wave[0];
 #pragma unroll
@@ -126,13 +122,6 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     };
     W prefix = id;
     if (tile > 0) {
-      bool agg_published = false;
-      auto idle = [&]() {
-        if (!agg_published && posted()) {
-          if (lane == 0) Desc<W>::publish(desc, tile, kAgg, tile_agg());
-          agg_published = true;
-        }
-      };
       // fallback for a late predecessor: reduce its input in element order
       auto reduce_tile = [&](int64_t t) -> W {
         W acc = id;
@@ -151,9 +140,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
         }
         return acc;
       };
-      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile, idle);
+      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile);
     }
-    while (!posted()) __builtin_amdgcn_s_sleep(1);
+    while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
       Desc<W>::publish(desc, tile, kInc, combine<O>(prefix, tile_agg()));
       s_prefix = prefix;

@@ -12,9 +12,10 @@
 //      vector j*64 + l of its run) and the matching flag bytes, and forms a
 //      bit mask of its selected elements;
 //   2. lane counts are scanned across the wave (DPP) and posted to LDS; the
-//      look-back wave, walking back over the predecessors' descriptors from
-//      the start, publishes the tile's count once posted and then the tile's
-//      output offset G; the tile with the last id writes num_out;
+//      last data wave to post publishes the tile's count; the look-back wave,
+//      walking back over the predecessors' descriptors from the start, then
+//      publishes the tile's inclusive count and hands over the tile's output
+//      offset G; the tile with the last id writes num_out;
 //   3. selected elements are packed into LDS at their rank, shifted so LDS
 //      vectors line up with 16-byte vectors of `out`, and the workgroup
 //      stores the packed run [G, G + count) with 16-byte stores (element
@@ -50,11 +51,15 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   __shared__ uint32_t s_wave[WD];
   __shared__ uint32_t s_prefix;
   __shared__ uint32_t s_posted;   // data waves whose counts are in s_wave
+  __shared__ uint32_t s_agg_done; // the tile's count is published
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
-  if (threadIdx.x == 0) s_posted = 0u;
+  if (threadIdx.x == 0) {
+    s_posted = 0u;
+    s_agg_done = 0u;
+  }
   __syncthreads();
 
   // Flag bytes of the run of 64*K vectors starting at `first` (E bytes per
@@ -141,16 +146,13 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
       carry += readlane(incl, kWave - 1);
     }
     if (lane == 0) {
-      s_wave[wave] = carry;
-      __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      post_wave_total<Op::Add, uint32_t, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done,
+                                             desc);
     }
   } else {
-    // 2'. the look-back wave: walks back from the start, publishes the tile's
-    //     count as soon as all waves posted it, and the tile's output offset
-    auto posted = [&]() {
-      return __hip_atomic_load(&s_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
-             (uint32_t)WD;
-    };
+    // 2'. the look-back wave: walks back from the start and, once the last
+    //     data wave has published the tile's count, publishes the tile's
+    //     inclusive count and hands over the output offset
     auto tile_count = [&]() {
       uint32_t a = 0u;
 #pragma unroll
@@ -159,13 +161,6 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     };
     uint32_t prefix = 0u;
     if (tile > 0) {
-      bool agg_published = false;
-      auto idle = [&]() {
-        if (!agg_published && posted()) {
-          if (lane == 0) Desc<uint32_t>::publish(desc, tile, kAgg, tile_count());
-          agg_published = true;
-        }
-      };
       // fallback for a late predecessor: count its selected flags
       auto reduce_tile = [&](int64_t t) -> uint32_t {
         uint32_t acc = 0u;
@@ -180,9 +175,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
         }
         return acc;
       };
-      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile, idle);
+      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile);
     }
-    while (!posted()) __builtin_amdgcn_s_sleep(1);
+    while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
       const uint32_t agg = tile_count();
       Desc<uint32_t>::publish(desc, tile, kInc, prefix + agg);
