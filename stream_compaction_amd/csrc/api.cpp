@@ -94,7 +94,7 @@ size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype) {
   sca::Fmt fmt;
   size_t eb;
   if (!fmt_of(dtype, &fmt, &eb) || n < 0) return 0;
-  return round16(sca::scan_device_tiles(n, fmt) * sca::scan_device_desc_words(fmt) * 8);
+  return sca::desc_scratch_bytes(sca::scan_device_tiles(n, fmt));
 }
 
 static scan_status scan_device_any(const void* in, void* out, int64_t n, scan_dtype dtype,
@@ -161,7 +161,7 @@ scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype
 
 size_t reduce_by_key_scratch_bytes(int64_t n) {
   if (n < 0) return 0;
-  return round16(sca::reduce_by_key_tiles(n) * 4 * 8);
+  return sca::desc_scratch_bytes(sca::reduce_by_key_tiles(n));
 }
 
 scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys_out,
@@ -200,7 +200,7 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
 
 size_t select_compact_scratch_bytes(int64_t n) {
   if (n < 0) return 0;
-  return round16(sca::select_tiles(n, 8) * 8);
+  return sca::desc_scratch_bytes(sca::select_tiles(n, 8));
 }
 
 scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,

@@ -365,16 +365,24 @@ __device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Each tile's descriptor owns one 128-byte cache line (kDescLineWords words,
+// of which kWords are used).  With descriptors packed 8 bytes apart, the
+// tiles sharing a line contended for it while one wrote and many polled
+// (MI355X, 2^28 i32 scan: 381 us packed, 367 us one line per tile; select
+// of 2^28 f32 at p = 0.5: 406 us packed, 370 us per line).
+constexpr int64_t kDescLineWords = 16;
+
 template <class W, int SZ = sizeof(W)> struct Desc;
 
 template <class W> struct Desc<W, 4> {
   static constexpr int kWords = 1;
   static __device__ __forceinline__ void publish(uint64_t* d, int64_t tile, uint32_t status, W v) {
-    st_relaxed(d + tile, ((uint64_t)status << 32) | __builtin_bit_cast(uint32_t, v));
+    st_relaxed(d + tile * kDescLineWords,
+               ((uint64_t)status << 32) | __builtin_bit_cast(uint32_t, v));
   }
   // Returns the status; sets v when it is not kNone.
   static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
-    const uint64_t w = ld_relaxed(d + tile);
+    const uint64_t w = ld_relaxed(d + tile * kDescLineWords);
     v = __builtin_bit_cast(W, (uint32_t)w);
     return (uint32_t)(w >> 32);
   }
@@ -384,13 +392,13 @@ template <class W> struct Desc<W, 8> {
   static constexpr int kWords = 4;
   static __device__ __forceinline__ void publish(uint64_t* d, int64_t tile, uint32_t status, W v) {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    uint64_t* slot = d + tile * 4 + (status == kInc ? 2 : 0);
+    uint64_t* slot = d + tile * kDescLineWords + (status == kInc ? 2 : 0);
     st_relaxed(slot, (1ull << 32) | (uint32_t)u);
     st_relaxed(slot + 1, (1ull << 32) | (uint32_t)(u >> 32));
   }
   // All four words are loaded together (one round trip, not two).
   static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
-    const uint64_t* s = d + tile * 4;
+    const uint64_t* s = d + tile * kDescLineWords;
     const uint64_t alo = ld_relaxed(s), ahi = ld_relaxed(s + 1);
     const uint64_t ilo = ld_relaxed(s + 2), ihi = ld_relaxed(s + 3);
     if ((ilo >> 32) && (ihi >> 32)) {
@@ -453,24 +461,19 @@ __device__ __forceinline__ bool lds_flag_set(const uint32_t* p) {
 // needs nothing from workgroups that have not started, so it ends whatever
 // order the hardware runs workgroups in; in the usual case no descriptor is
 // that late and no tile is reduced twice.
-// Pauses between descriptor polls, in s_sleep units of 64 cycles (127: about
-// 8k cycles, ~3.4 us).  Polling is not free on MI355X: every poll is a
-// device-scope read that goes past the XCD's L2, and with hundreds of tiles
-// waiting at once short pauses between window polls measurably slow the data
-// traffic (2^28 i32 scan: 419 us with a window pause of 16, 410 us at 32,
-// 385 us at 127).  The pre-wait polls one descriptor, and its pause length
-// made no measurable difference (2: 388 us, 127: 385 us).  Both can be
-// overridden at compile time for measurements.
-#ifndef SCA_PREWAIT_SLEEP
-#define SCA_PREWAIT_SLEEP 127
-#endif
-#ifndef SCA_WINDOW_SLEEP
-#define SCA_WINDOW_SLEEP 127
-#endif
-constexpr int kPreWaitSleep = SCA_PREWAIT_SLEEP;
-constexpr int kPollSleep = SCA_WINDOW_SLEEP;
+// Pause between two polls of a single descriptor (template argument PAUSE of
+// look_back), in s_sleep units of 64 cycles.  The look-back only ever waits
+// on one descriptor at a time (the nearest predecessor first, then the
+// nearest one a window still lacks), so a poll is one load per wave, and
+// windows of 64 descriptors are read only when the awaited one has arrived.
+// Even so, frequent polls by hundreds of waiting tiles slow kernels whose
+// tiles live long (2^28 i32 scan: 385 us at a pause of 8, 367 us at 127),
+// while kernels with short-lived tiles need the finer wake-up (reduce-by-key
+// of 2^27 pairs: 456 us at 8, 508 us at 127); each kernel passes its own.
+constexpr int kPollLong = 127;   // about 8k cycles, ~3.4 us
+constexpr int kPollShort = 8;    // about 512 cycles, ~0.2 us
 
-template <Op O, class W, class ReduceTile>
+template <Op O, class W, int PAUSE, class ReduceTile>
 __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint64_t timeout,
                                        ReduceTile&& reduce_tile) {
   const int lane = lane_id();
@@ -483,9 +486,8 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     W v;
     while (Desc<W>::read(desc, tile - 1, v) == kNone &&
-           __builtin_amdgcn_s_memrealtime() - t0 <= timeout) {
-      __builtin_amdgcn_s_sleep(kPreWaitSleep);
-    }
+           __builtin_amdgcn_s_memrealtime() - t0 <= timeout)
+      __builtin_amdgcn_s_sleep(PAUSE);
   }
   for (int64_t base = tile - 1;; base -= kWave) {
     const int64_t t = base - (kWave - 1) + lane;
@@ -512,7 +514,13 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
         }
         break;
       }
-      __builtin_amdgcn_s_sleep(kPollSleep);
+      // wait on the nearest missing descriptor alone (one load per poll),
+      // then read the whole window again
+      const int64_t tl = base - (kWave - 1) + (63 - __builtin_clzll(pending));
+      W u;
+      while (Desc<W>::read(desc, tl, u) == kNone &&
+             __builtin_amdgcn_s_memrealtime() - t0 <= timeout)
+        __builtin_amdgcn_s_sleep(PAUSE);
     }
     const uint64_t inc = __ballot(st == kInc);
     const int stop = inc ? 63 - __builtin_clzll(inc) : 0;

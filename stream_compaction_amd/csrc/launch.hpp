@@ -20,7 +20,6 @@ hipError_t launch_scan_rows(const void* in, void* out, int64_t rows, int64_t n, 
 
 // Device-wide exclusive (or inclusive) scan; op: 0 add, 1 min, 2 max.
 size_t scan_device_tiles(int64_t n, Fmt fmt);       // descriptors needed
-size_t scan_device_desc_words(Fmt fmt);             // 64-bit words per descriptor
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
                               bool inclusive, void* scratch, hipStream_t stream);
 
@@ -42,11 +41,19 @@ size_t select_tiles(int64_t n, size_t elem_bytes);
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                          int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream);
 
-// Scratch of the look-back kernels holds only the tile descriptor words
-// (zeroed at the start of every call).
-// Zero `bytes` rounded up to a multiple of 16 at a 16-byte-aligned device
-// address (scratch sizes are rounded the same way) with a small fill kernel
-// (no hipMemsetAsync, so the call can sit in a captured graph).
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Scratch of the look-back kernels holds only the tile descriptors, one per
+// 128-byte line (kDescBytes), whose used words are zeroed at the start of
+// every call by a small fill kernel (no hipMemsetAsync, so the call can sit
+// in a captured graph).
+// The descriptors start at the first 128-byte boundary of the caller's
+// (16-byte aligned) scratch, so scratch sizes carry one line of slack.
+constexpr size_t kDescBytes = 128;
+inline size_t desc_scratch_bytes(size_t ntiles) {
+  return ntiles == 0 ? 0 : ntiles * kDescBytes + kDescBytes;
+}
+inline uint64_t* desc_base(void* scratch) {
+  return (uint64_t*)(((uintptr_t)scratch + kDescBytes - 1) & ~(uintptr_t)(kDescBytes - 1));
+}
+hipError_t launch_fill_desc(uint64_t* desc, int64_t ntiles, int words, hipStream_t stream);
 
 }  // namespace sca

@@ -31,7 +31,9 @@
 
 namespace sca {
 
-constexpr int64_t kRbkMinTileVecs = 512;
+// Smallest tile (in vectors) of any launch shape below (7 data waves x 8
+// loads x 64 lanes); scratch is sized for it.
+constexpr int64_t kRbkMinTileVecs = 3584;
 
 // The scan state of a span: run starts in it and the sum after the last one.
 // V is float for f32 values and uint32_t for i32/u32 values (wrapping).
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
         }
         return acc;
       };
-      prefix = look_back<Op::Add, W>(desc, tile, kLookBackTimeout, reduce_tile);
+      prefix = look_back<Op::Add, W, kPollShort>(desc, tile, kLookBackTimeout, reduce_tile);
     }
     while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
@@ -259,16 +261,17 @@ static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* key
   const int e = vec ? 4 : 1;
   const int64_t ph = vec ? (int64_t)((ka % 16) / 4) : 0;
   const int64_t ntiles = rbk_tiles_for(n, e, TV);
-  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * 4 * 8, stream);
+  uint64_t* desc = desc_base(scratch);
+  hipError_t err = launch_fill_desc(desc, ntiles, Desc<Seg<float>>::kWords, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ko = (uintptr_t)keys_out, vo = (uintptr_t)values_out, nr = (uintptr_t)num_runs;
   if (vec) {
     reduce_by_key_kernel<KF, VF, 4, WD, K><<<grid, block, 0, stream>>>(
-        ka - ph * 4, va - ph * 4, n, ph, ntiles, ko, vo, nr, (uint64_t*)scratch);
+        ka - ph * 4, va - ph * 4, n, ph, ntiles, ko, vo, nr, desc);
   } else {
     reduce_by_key_kernel<KF, VF, 1, WD, K><<<grid, block, 0, stream>>>(
-        ka, va, n, 0, ntiles, ko, vo, nr, (uint64_t*)scratch);
+        ka, va, n, 0, ntiles, ko, vo, nr, desc);
   }
   return hipGetLastError();
 }

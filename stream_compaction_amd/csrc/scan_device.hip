@@ -31,8 +31,9 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
-constexpr int64_t kDevMinTileVecs = 512;
+// Smallest tile (in vectors) of any launch shape below (7 data waves x 16
+// loads x 64 lanes); scratch is sized for it.
+constexpr int64_t kDevMinTileVecs = 7168;
 
 template <class F, Op O, bool INCL, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
         }
         return acc;
       };
-      prefix = look_back<O, W>(desc, tile, kLookBackTimeout, reduce_tile);
+      prefix = look_back<O, W, kPollLong>(desc, tile, kLookBackTimeout, reduce_tile);
     }
     while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
@@ -167,7 +168,6 @@ static int fmt_bytes(Fmt f) {
   }
 }
 
-size_t scan_device_desc_words(Fmt fmt) { return fmt_bytes(fmt) == 8 ? 4 : 1; }
 
 // Sized for the slowest path (one element per vector) and the smallest tile,
 // so one scratch size serves every pointer alignment and launch shape.
@@ -185,13 +185,12 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   constexpr int EV = 16 / (int)sizeof(S);
   constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
-  uint64_t* desc = (uint64_t*)scratch;
+  uint64_t* desc = desc_base(scratch);
   const bool vec = (ia % 16) == (oa % 16);
   const int e = vec ? EV : 1;
   const int64_t ph = vec ? (int64_t)((ia % 16) / sizeof(S)) : 0;
   const int64_t ntiles = tiles_for(n, e, TV);
-  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * Desc<typename F::W>::kWords * 8,
-                                    stream);
+  hipError_t err = launch_fill_desc(desc, ntiles, Desc<typename F::W>::kWords, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   if (vec) {
@@ -239,20 +238,22 @@ hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int
 }
 
 // ---------------------------------------------------------------------------
-// Small fill kernel used to reset scratch at the start of each call.
+// Small kernel that resets the used words of `ntiles` descriptors (one per
+// 128-byte line) at the start of each call.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+__global__ __launch_bounds__(256) void fill_desc_kernel(uint64_t* d, int64_t ntiles, int words) {
+  const int64_t total = ntiles * words;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = uint4{0u, 0u, 0u, 0u};
+    d[(i / words) * kDescLineWords + i % words] = 0ull;
 }
 
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
-  const int64_t n16 = (int64_t)((bytes + 15) / 16);
-  if (n16 == 0) return hipSuccess;
-  int64_t blocks = (n16 + kBlock - 1) / kBlock;
+hipError_t launch_fill_desc(uint64_t* desc, int64_t ntiles, int words, hipStream_t stream) {
+  const int64_t total = ntiles * words;
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + kBlock - 1) / kBlock;
   if (blocks > 2048) blocks = 2048;
-  fill_zero_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>((uint4*)p, n16);
+  fill_desc_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(desc, ntiles, words);
   return hipGetLastError();
 }
 

@@ -27,8 +27,9 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below; scratch is sized for it.
-constexpr int64_t kSelMinTileVecs = 512;
+// Smallest tile (in vectors) of any launch shape below (3 data waves x 12
+// loads x 64 lanes); scratch is sized for it.
+constexpr int64_t kSelMinTileVecs = 2304;
 
 template <int EB> struct Bits;
 template <> struct Bits<4> { using T = uint32_t; };
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
         }
         return acc;
       };
-      prefix = look_back<Op::Add, uint32_t>(desc, tile, kLookBackTimeout, reduce_tile);
+      prefix = look_back<Op::Add, uint32_t, kPollLong>(desc, tile, kLookBackTimeout, reduce_tile);
     }
     while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
@@ -255,8 +256,8 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
   const uintptr_t fbase = fa - (uintptr_t)ph;          // flag byte of window element 0
   const bool fvec = (fbase % E) == 0;
   const int64_t ntiles = sel_tiles_for(n, E, TV);
-  uint64_t* desc = (uint64_t*)scratch;
-  hipError_t err = launch_fill_zero(scratch, (size_t)ntiles * 8, stream);
+  uint64_t* desc = desc_base(scratch);
+  hipError_t err = launch_fill_desc(desc, ntiles, Desc<uint32_t>::kWords, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ibase = ia - (uintptr_t)ph * EB, obase = oa - (uintptr_t)out_ph * EB;
