@@ -24,6 +24,9 @@ computes, with the passages it follows:
 * ``reduce_by_key``: runs of equal consecutive keys collapsed into (first key,
   sum of values) per the "Algorithms" page, section
   ``qd.algorithms.reduce_by_key_add``.
+* ``sort`` / ``sort_image``: stable ascending radix-sort order per the
+  "Algorithms" page, section ``qd.algorithms.sort`` (sortable-key transform
+  written out; numpy's stable argsort orders the transformed keys).
 * ``select``: stream compaction per the "Algorithms" page, section
   ``qd.algorithms.select`` (stable, dense prefix, count).
 * ``f32_to_bf16`` / ``f32_to_f16`` and the widenings: round-to-nearest-even per
@@ -169,6 +172,51 @@ def reduce_by_key(keys, values, key_dtype, value_dtype, want_ref=False):
     if want_ref:
         return ko, vo, int(r), ref, absref
     return ko, vo, int(r)
+
+
+_SORT_UNSIGNED = {"u32": np.uint32, "i32": np.uint32, "f32": np.uint32,
+                  "u64": np.uint64, "i64": np.uint64, "f64": np.uint64}
+
+
+def sort_image(keys, key_dtype, end_bit=None):
+    """The unsigned integer each key sorts by (ascending), restricted to its
+    low ``end_bit`` bits.
+
+    Written from the "Algorithms" page, section qd.algorithms.sort (Under the
+    hood): unsigned keys sort as they are; signed keys with their sign bit
+    flipped; floats with the sign bit flipped when it is clear and every bit
+    flipped when it is set (the standard sortable-key transform), so -0 sorts
+    just before +0.  The page also states that NaNs land at the end, as in
+    numpy.sort: every NaN (either sign) takes the largest image, so NaNs go
+    last and keep their input order.
+    """
+    u_t = _SORT_UNSIGNED[key_dtype]
+    bits = 32 if u_t is np.uint32 else 64
+    u = np.ascontiguousarray(keys).view(u_t).copy()
+    top = u_t(1) << u_t(bits - 1)
+    if key_dtype in ("i32", "i64"):
+        u ^= top
+    elif key_dtype in ("f32", "f64"):
+        neg = (u & top) != 0
+        u = np.where(neg, ~u, u | top).astype(u_t)
+        f = np.ascontiguousarray(keys).view(np.float32 if bits == 32 else np.float64)
+        u[np.isnan(f)] = np.iinfo(u_t).max
+    if end_bit is not None and end_bit < bits:
+        u &= u_t((1 << end_bit) - 1)
+    return u
+
+
+def sort(keys, key_dtype, values=None, end_bit=None):
+    """Stable ascending sort of 1-D ``keys`` by their sort image (see
+    ``sort_image``); ``values`` (any 1-D array of the same length) are
+    permuted alongside.  The "Algorithms" page, section qd.algorithms.sort:
+    ascending, stable (equal images keep their input order).  Returns
+    ``(sorted_keys, sorted_values or None)``; the keys' bits are moved, not
+    transformed.  The ordering step is numpy's stable argsort of the images.
+    """
+    keys = np.ascontiguousarray(keys)
+    order = np.argsort(sort_image(keys, key_dtype, end_bit), kind="stable")
+    return keys[order], (None if values is None else np.ascontiguousarray(values)[order])
 
 
 def select(x, flags):

@@ -612,3 +612,98 @@ def test_reduce_by_key_f32_values_double_sum():
         exact = math.fsum(seg)
         assert abs(ref[j] - exact) <= 1000 * 2.0 ** -53 * absref[j]
         assert vo[j] == np.float32(ref[j])
+
+
+# ---- radix-sort order ----------------------------------------------------------------------------
+
+def test_page_sort_example(golden):
+    g = golden("sort_example.json")
+    k, v = oracle.sort(np.array(g["keys"], np.int32), "i32", np.array(g["values"], np.int32))
+    assert k.tolist() == g["sorted_keys"] and v.tolist() == g["sorted_values"]
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "i64", "u64"])
+def test_sort_ints_match_numpy_stable(dt):
+    rng = np.random.default_rng(51)
+    t = INT_DT[dt]
+    info = np.iinfo(t)
+    for n, hi in ((10000, None), (10000, 7)):           # full range, and many duplicates
+        x = (rng.integers(info.min, info.max, size=n, endpoint=True, dtype=t) if hi is None else
+             rng.integers(0, hi, size=n).astype(t))
+        idx = np.arange(n, dtype=np.int64)
+        k, v = oracle.sort(x, dt, idx)
+        want = np.argsort(x, kind="stable")                # numpy compares the native integers
+        assert np.array_equal(v, want) and np.array_equal(k, x[want])
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_sort_floats_match_numpy_without_nan_or_zero(dt):
+    rng = np.random.default_rng(52)
+    f = np.float32 if dt == "f32" else np.float64
+    x = rng.choice(rng.standard_normal(300).astype(f), size=20000)        # duplicates, no zeros
+    x[::97] = np.inf
+    x[::89] = -np.inf
+    idx = np.arange(x.size)
+    k, v = oracle.sort(x, dt, idx)
+    want = np.argsort(x, kind="stable")
+    assert np.array_equal(v, want)
+
+
+def _brute_sort_key(x):
+    """An independent statement of the order: NaNs last; otherwise by value,
+    with -0 before +0."""
+    xf = float(x)
+    if math.isnan(xf):
+        return (1, 0.0, 0)
+    return (0, xf, 0 if (xf == 0.0 and math.copysign(1.0, xf) < 0) else 1)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_sort_floats_brute_force_specials(dt):
+    f = np.float32 if dt == "f32" else np.float64
+    alphabet = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, -np.nan, 1.5, -1.5, 3.0], f)
+    rng = np.random.default_rng(53)
+    for n in range(0, 40):
+        x = alphabet[rng.integers(0, alphabet.size, size=n)]
+        idx = np.arange(n)
+        k, v = oracle.sort(x, dt, idx)
+        want = sorted(range(n), key=lambda i: _brute_sort_key(x[i]))    # Python's sort is stable
+        assert v.tolist() == want, (n, x)
+        assert k.view(np.uint8).tobytes() == x[want].view(np.uint8).tobytes()   # bits moved intact
+
+
+def test_sort_signed_zero_and_nan_order():
+    nan_p = np.float32(np.nan)
+    nan_n = np.array([0xffc00001], np.uint32).view(np.float32)[0]
+    x = np.array([0.0, -0.0, nan_n, 1.0, nan_p, -0.0, -np.inf, 0.0], np.float32)
+    k, v = oracle.sort(x, "f32", np.arange(8))
+    assert v.tolist() == [6, 1, 5, 0, 7, 3, 2, 4]
+
+
+def test_sort_end_bit_uses_low_bits_only():
+    rng = np.random.default_rng(54)
+    x = rng.integers(0, 1 << 32, size=5000, dtype=np.uint64).astype(np.uint32)
+    for end_bit in (8, 16, 24):
+        k, v = oracle.sort(x, "u32", np.arange(x.size), end_bit=end_bit)
+        want = np.argsort(x & np.uint32((1 << end_bit) - 1), kind="stable")
+        assert np.array_equal(v, want)
+    # i32 with end_bit 32 is the full signed order; with fewer bits the sign flip is masked away
+    y = rng.integers(-1000, 1000, size=3000).astype(np.int32)
+    _, v = oracle.sort(y, "i32", np.arange(y.size), end_bit=16)
+    want = np.argsort((y.view(np.uint32) ^ np.uint32(1 << 31)) & np.uint32(0xffff), kind="stable")
+    assert np.array_equal(v, want)
+
+
+@pytest.mark.parametrize("dt", ["u32", "i32", "f32", "u64", "i64", "f64"])
+def test_sort_output_is_sorted_permutation(dt):
+    rng = np.random.default_rng(55)
+    raw = rng.integers(0, 256, size=8 * 5000, dtype=np.uint8)
+    x = raw.view(oracle.STORAGE[dt])[:5000].copy()        # arbitrary bit patterns, NaNs included
+    k, v = oracle.sort(x, dt, np.arange(x.size))
+    img = oracle.sort_image(k, dt)
+    assert (np.diff(img.astype(object) if img.dtype == np.uint64 else img.astype(np.int64)) >= 0).all()
+    assert sorted(v.tolist()) == list(range(x.size))
+    assert np.array_equal(k.view(np.uint8), x[v].view(np.uint8))
+    # stability: equal images keep increasing original positions
+    same = img[1:] == img[:-1]
+    assert (v[1:][same] > v[:-1][same]).all()
