@@ -1,8 +1,8 @@
 /*
  * scan.h - C ABI of the stream_compaction_amd library (libscan_amd.so):
  * row-wise prefix scan, device-wide exclusive and inclusive scan, device-wide
- * reduction, reduce-by-key and stream compaction on one AMD Instinct MI355X
- * (gfx950).
+ * reduction, reduce-by-key, radix sort and stream compaction on one AMD
+ * Instinct MI355X (gfx950).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -176,6 +176,37 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
                           void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
                           scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
                           void* stream);
+
+/*
+ * Radix sort ("Algorithms" page, section qd.algorithms.sort): stable ascending
+ * LSD radix sort, 8-bit digits, of n keys in place in `keys`, carrying
+ * `values` along when given.  The order is that of each key's sortable image
+ * (unsigned keys as they are; signed keys with the sign bit flipped; floats
+ * with the sign bit flipped when clear and every bit flipped when set, so
+ * -0 sorts before +0), restricted to its low `end_bit` bits; every NaN key
+ * sorts after all other keys, in input order (the page's "NaNs land at the
+ * end").  Equal images keep their input order.  Keys and values move as raw
+ * bits.
+ *
+ *   keys, tmp_keys       device pointers, n keys of key_dtype each, distinct;
+ *                        tmp_keys holds garbage on return.
+ *   values, tmp_values   both NULL (keys-only sort) or both device pointers to
+ *                        n values of value_dtype each, distinct.
+ *   key_dtype            SCAN_U32, SCAN_I32, SCAN_F32, SCAN_U64, SCAN_I64 or
+ *                        SCAN_F64 (else SCAN_ENOTSUP).
+ *   value_dtype          any of the same six (ignored for a keys-only sort).
+ *   end_bit              a multiple of 8 in [8, key bits] (else SCAN_EINVAL);
+ *                        end_bit / 8 digit passes.
+ *   n                    0 <= n < 2^30 (else SCAN_EINVAL: the per-tile digit
+ *                        counts travel in 30-bit words).
+ *   scratch              >= radix_sort_scratch_bytes(n, key_dtype) bytes,
+ *                        16-byte aligned; needs no initialization.
+ * No two of keys, tmp_keys, values, tmp_values and scratch may overlap.
+ */
+size_t radix_sort_scratch_bytes(int64_t n, scan_dtype key_dtype);
+scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
+                       scan_dtype key_dtype, scan_dtype value_dtype, int end_bit, void* scratch,
+                       size_t scratch_bytes, void* stream);
 
 /*
  * Stream compaction ("Algorithms" page, section qd.algorithms.select): every

@@ -19,6 +19,9 @@ Entry points (same names as the C ABI):
   reduction into a 1-element GPU tensor.
 * ``reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None,
   scratch=None)`` - runs of equal consecutive keys collapsed into (key, sum).
+* ``radix_sort(keys, values=None, tmp_keys=None, tmp_values=None, end_bit=None,
+  scratch=None)`` - stable ascending sort of a 1-D tensor of 32/64-bit keys in
+  place, carrying values along.
 * ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
   stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
 * ``scan_device_scratch_bytes(n, dtype)``, ``reduce_device_scratch_bytes(n,
@@ -37,8 +40,9 @@ DTYPE_CODES = {"f32": 1, "f16": 2, "bf16": 3, "f64": 4, "i32": 5, "u32": 6, "i64
 OP_CODES = {"add": 1, "min": 2, "max": 3, "mul": 4}
 EXPORTS = ("scan_rows", "scan_device", "scan_device_inclusive", "scan_device_scratch_bytes",
            "reduce_device", "reduce_device_scratch_bytes", "reduce_by_key",
-           "reduce_by_key_scratch_bytes", "select_compact", "select_compact_scratch_bytes",
-           "scan_status_str", "scan_last_hip_error")
+           "reduce_by_key_scratch_bytes", "radix_sort", "radix_sort_scratch_bytes",
+           "select_compact", "select_compact_scratch_bytes", "scan_status_str",
+           "scan_last_hip_error")
 
 _lib = None
 
@@ -78,6 +82,10 @@ def load(path):
     L.reduce_by_key_scratch_bytes.restype = sz
     L.reduce_by_key.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, sz, vp]
     L.reduce_by_key.restype = i32
+    L.radix_sort_scratch_bytes.argtypes = [i64, i32]
+    L.radix_sort_scratch_bytes.restype = sz
+    L.radix_sort.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    L.radix_sort.restype = i32
     L.select_compact_scratch_bytes.argtypes = [i64]
     L.select_compact_scratch_bytes.restype = sz
     L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
@@ -252,6 +260,42 @@ def reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None, s
                               _dev_ptr(num_runs, "num_runs"), n, DTYPE_CODES[kd], DTYPE_CODES[vd],
                               _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
     return keys_out, values_out, num_runs
+
+
+def radix_sort_scratch_bytes(n, key_dtype):
+    name = key_dtype if isinstance(key_dtype, str) else dtype_name(key_dtype)
+    return int(lib().radix_sort_scratch_bytes(int(n), DTYPE_CODES[name]))
+
+
+def radix_sort(keys, values=None, tmp_keys=None, tmp_values=None, end_bit=None, scratch=None,
+               stream=None, key_dtype=None, value_dtype=None):
+    """Stable ascending radix sort of the 1-D ``keys`` in place (``values`` in place
+    alongside).  Returns ``(keys, values)``."""
+    torch = _torch()
+    if keys.dim() != 1:
+        raise ValueError("keys must be 1-D")
+    n = keys.shape[0]
+    kd = _name(keys, key_dtype)
+    if end_bit is None:
+        end_bit = 8 * keys.element_size()
+    if tmp_keys is None:
+        tmp_keys = torch.empty_like(keys)
+    vd = 0
+    vptr = tvptr = None
+    if values is not None:
+        if values.dim() != 1 or values.shape[0] != n:
+            raise ValueError("values must be 1-D with one value per key")
+        vd = DTYPE_CODES[_name(values, value_dtype)]
+        if tmp_values is None:
+            tmp_values = torch.empty_like(values)
+        vptr, tvptr = _dev_ptr(values, "values"), _dev_ptr(tmp_values, "tmp_values")
+    need = radix_sort_scratch_bytes(n, kd)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=keys.device)
+    check(lib().radix_sort(_dev_ptr(keys, "keys"), _dev_ptr(tmp_keys, "tmp_keys"), vptr, tvptr, n,
+                           DTYPE_CODES[kd], vd, int(end_bit), _dev_ptr(scratch, "scratch"),
+                           scratch.numel(), _stream(stream)))
+    return keys, values
 
 
 def select_compact_scratch_bytes(n):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libscan_amd.so")
 SOURCES = ["scan_rows.hip", "scan_device.hip", "select.hip", "reduce.hip", "reduce_by_key.hip",
-           "api.cpp"]
+           "radix_sort.hip", "api.cpp"]
 # measurement aid for the benchmark (16-byte copy kernel), kept out of the scan library
 COPY_LIB_PATH = os.path.join(HERE, "libscan_copy.so")
 COPY_SOURCES = ["copy_ceiling.hip"]

@@ -52,6 +52,7 @@ scan_status hip_status(hipError_t e) {
 }
 
 constexpr int64_t kMaxN = 2147483647;  // INT32_MAX
+constexpr int64_t kMaxSortN = int64_t(1) << 30;   // radix-sort counts are 30-bit
 
 }  // namespace
 
@@ -196,6 +197,41 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
   }
   return hip_status(sca::launch_reduce_by_key(keys_in, values_in, keys_out, values_out, num_runs,
                                               n, kf, vf, scratch, (hipStream_t)stream));
+}
+
+size_t radix_sort_scratch_bytes(int64_t n, scan_dtype key_dtype) {
+  sca::Fmt f;
+  size_t eb;
+  if (!fmt_of(key_dtype, &f, &eb) || eb < 4 || n < 0) return 0;
+  return round16(sca::radix_sort_scratch(n, eb));
+}
+
+scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
+                       scan_dtype key_dtype, scan_dtype value_dtype, int end_bit, void* scratch,
+                       size_t scratch_bytes, void* stream) {
+  sca::Fmt kf, vf;
+  size_t keb, veb = 0;
+  if (!fmt_of(key_dtype, &kf, &keb) || keb < 4) return SCAN_ENOTSUP;
+  if (values != nullptr || tmp_values != nullptr) {
+    if (!fmt_of(value_dtype, &vf, &veb) || veb < 4) return SCAN_ENOTSUP;
+    if (values == nullptr || tmp_values == nullptr) return SCAN_EINVAL;
+  }
+  if (n < 0 || n >= kMaxSortN) return SCAN_EINVAL;
+  if (end_bit < 8 || end_bit > (int)(8 * keb) || end_bit % 8 != 0) return SCAN_EINVAL;
+  if (n <= 1) return SCAN_OK;
+  if (keys == nullptr || tmp_keys == nullptr || scratch == nullptr) return SCAN_EINVAL;
+  if (!aligned(keys, keb) || !aligned(tmp_keys, keb) || !aligned(scratch, 16)) return SCAN_EINVAL;
+  if (veb && (!aligned(values, veb) || !aligned(tmp_values, veb))) return SCAN_EINVAL;
+  const size_t need = radix_sort_scratch_bytes(n, key_dtype);
+  if (scratch_bytes < need) return SCAN_ESCRATCH;
+  const size_t kb = (size_t)n * keb, vb = (size_t)n * veb;
+  const void* r[5] = {keys, tmp_keys, values, tmp_values, scratch};
+  const size_t z[5] = {kb, kb, vb, vb, need};
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (overlap(r[a], z[a], r[b], z[b])) return SCAN_EALIAS;
+  return hip_status(sca::launch_radix_sort(keys, tmp_keys, values, tmp_values, n, kf, (int)veb,
+                                           end_bit, scratch, (hipStream_t)stream));
 }
 
 size_t select_compact_scratch_bytes(int64_t n) {

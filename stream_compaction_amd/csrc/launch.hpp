@@ -36,6 +36,12 @@ hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys
                                 void* values_out, int32_t* num_runs, int64_t n, Fmt kfmt,
                                 Fmt vfmt, void* scratch, hipStream_t stream);
 
+// Radix sort (n < 2^30); value_bytes 0 (keys only), 4 or 8.
+size_t radix_sort_scratch(int64_t n, size_t key_bytes);
+hipError_t launch_radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
+                             Fmt kfmt, int value_bytes, int end_bit, void* scratch,
+                             hipStream_t stream);
+
 // Stream compaction.
 size_t select_tiles(int64_t n, size_t elem_bytes);
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,

@@ -210,3 +210,34 @@ def test_reduce_by_key_validation():
     assert call(s=V + 64) == EALIAS                   # scratch inside values_in
     # (calls that pass validation would launch on these fake addresses, so the
     # accepted cases, aliased inputs and n == 0 included, run in the GPU tests)
+
+
+def test_radix_sort_validation():
+    L = sc.lib()
+    n = 100_000
+    u32, u64 = D["u32"], D["u64"]
+    need = L.radix_sort_scratch_bytes(n, u32)
+    assert need > 0 and need % 16 == 0
+    assert L.radix_sort_scratch_bytes(n, D["bf16"]) == 0
+    KEY, TK, V, TV = A, A + 0x100000, B, B + 0x100000
+
+    def call(*, k=KEY, tk=TK, v=V, tv=TV, nn=n, kd=u32, vd=u32, eb=32, s=S, sb=need):
+        return L.radix_sort(k, tk, v, tv, nn, kd, vd, eb, s, sb, None)
+    assert call(kd=D["f16"]) == ENOTSUP
+    assert call(vd=D["bf16"]) == ENOTSUP
+    assert call(nn=-1) == EINVAL
+    assert call(nn=1 << 30) == EINVAL                 # counts travel in 30 bits
+    assert call(eb=12) == EINVAL
+    assert call(eb=0) == EINVAL
+    assert call(eb=40) == EINVAL                      # beyond a 32-bit key
+    assert call(v=None) == EINVAL                     # values without temporaries
+    assert call(k=None) == EINVAL
+    assert call(k=KEY + 2) == EINVAL
+    assert call(s=S + 8) == EINVAL
+    assert call(sb=need - 16) == ESCRATCH
+    assert call(tk=KEY + 400) == EALIAS
+    assert call(tv=V + 4) == EALIAS
+    assert call(s=TK + 64) == EALIAS
+    assert call(kd=u64, tk=KEY + 8 * n - 8, sb=L.radix_sort_scratch_bytes(n, u64)) == EALIAS
+    # 64-bit keys take 8 passes and have their own tile size
+    assert L.radix_sort_scratch_bytes(n, u64) > 0

@@ -25,12 +25,15 @@ for bf16, so that 8192-long products neither overflow nor underflow; the
 device-wide inclusive scans and the reductions reuse the inputs of workloads
 3 and 4 (plus an f32 add reduction of workload 4's f32 input); reduce-by-key
 runs on n = 2^27 i32 keys in runs of geometric length with mean 8 (each run's
-key uniform in [0, 2^20), seed 13) and f32 values uniform [0, 1) (seed 14).
+key uniform in [0, 2^20), seed 13) and f32 values uniform [0, 1) (seed 14);
+the radix sort on n = 2^28 u32 keys uniform over all 2^32 values (seed 15),
+keys only and with i32 values (each key's original index).
 """
 import numpy as np
 
 SEEDS = {"rows_f32": 0, "rows_bf16": 1, "dev_i32": 2, "dev_f32": 3, "dev_i64": 4,
-         "sel_payload": 5, "prod_f32": 11, "prod_bf16": 12, "rbk_keys": 13, "rbk_values": 14}
+         "sel_payload": 5, "prod_f32": 11, "prod_bf16": 12, "rbk_keys": 13, "rbk_values": 14,
+         "sort_keys": 15}
 
 FULL = {
     "rows_f32": (1024, 4096),
@@ -42,6 +45,7 @@ FULL = {
     "dev_i64": 1 << 26,
     "sel": 1 << 28,
     "rbk": 1 << 27,
+    "sort": 1 << 28,
 }
 RBK_MEAN_RUN = 8
 SELECT_P = (0.01, 0.5, 0.99)
@@ -155,3 +159,8 @@ def run_keys(n, mean_run, seed, key_range=1 << 20):
 def rbk_inputs(n=FULL["rbk"]):
     keys = run_keys(n, RBK_MEAN_RUN, SEEDS["rbk_keys"])
     return keys, payload_f32(n, SEEDS["rbk_values"])
+
+
+def sort_keys_u32(n=FULL["sort"], seed=SEEDS["sort_keys"]):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
