@@ -11,7 +11,7 @@ to nearest even).  Consecutive steps rotate over several input/output buffer
 pairs so that no step finds its data in the 256 MB Infinity Cache left there
 by the previous one.  The other workloads (row scans of fp32 [1024, 4096] and
 bf16 [8192, 8191], the bf16 product scan, the device-wide exclusive and
-inclusive scans, the reductions, reduce-by-key and select) are timed the same way and
+inclusive scans, the reductions, reduce-by-key, the radix sort and select) are timed the same way and
 reported inside the same JSON line under "workloads".
 
 Prints ONE JSON line.  "value" is elements/s of the headline workload (wall
@@ -40,6 +40,7 @@ KERNEL_SOURCES = {           # sources whose change invalidates stored counter r
     "select": ["device.hpp", "select.hip"],
     "reduce": ["device.hpp", "reduce.hip"],
     "reduce_by_key": ["device.hpp", "reduce_by_key.hip"],
+    "radix_sort": ["device.hpp", "radix_sort.hip"],
 }
 
 
@@ -333,6 +334,41 @@ def main():
                    "+ 8 per run written + 4; includes the descriptor-reset fill kernel")
         r["runs"] = runs
         del kd, vd, ko, vo
+    for name, with_vals in (("sort_u32", False), ("sort_u32_kv", True)):
+        if not want(name):
+            continue
+        # the sort works in place, so every call starts from a fresh copy of the
+        # unsorted keys, made before the call's own pair of HIP events
+        ns = wl.FULL["sort"]
+        k0 = torch.from_numpy(wl.sort_keys_u32(ns).view(np.int32)).to(dev)
+        kk, tk = torch.empty_like(k0), torch.empty_like(k0)
+        v0 = torch.arange(ns, dtype=torch.int32, device=dev) if with_vals else None
+        vv = torch.empty_like(k0) if with_vals else None
+        tv = torch.empty_like(k0) if with_vals else None
+        scr = torch.empty(sc.radix_sort_scratch_bytes(ns, "u32"), dtype=torch.uint8, device=dev)
+        per = []
+        cur = torch.cuda.current_stream()
+        t_all = 0.0
+        for i in range(W + K):
+            kk.copy_(k0)
+            if with_vals:
+                vv.copy_(v0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            sc.radix_sort(kk, vv, tk, tv, 32, scr, key_dtype="u32", value_dtype="i32")
+            e1.record(cur)
+            torch.cuda.synchronize()
+            if i >= W:
+                per.append(e0.elapsed_time(e1))
+                t_all += per[-1] * 1e-3
+        eb = 8 if with_vals else 4                      # bytes moved per element per pass, each way
+        record(name, ns, 4 * 2 * eb * ns + 4 * ns, t_all, per, K,
+               "2^28 uniform u32 keys" + (" with i32 values" if with_vals else ", keys only") +
+               "; algorithmic bytes = 4 passes x (read + write of keys" +
+               (" and values" if with_vals else "") + ") + one read of the keys for the "
+               "digit histograms; eager calls, each after an untimed copy of the unsorted input")
+        results[name]["keys_per_s"] = ns / float(np.mean(per) * 1e-3)
+        del k0, kk, tk, v0, vv, tv
     nsel = wl.FULL["sel"]
     for p in wl.SELECT_P:
         name = f"select_p{p}"

@@ -186,7 +186,8 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
  * -0 sorts before +0), restricted to its low `end_bit` bits; every NaN key
  * sorts after all other keys, in input order (the page's "NaNs land at the
  * end").  Equal images keep their input order.  Keys and values move as raw
- * bits.
+ * bits.  Each pass is the page's tile histogram, scan of the digit-major
+ * histograms (this library's device-wide scan) and scatter.
  *
  *   keys, tmp_keys       device pointers, n keys of key_dtype each, distinct;
  *                        tmp_keys holds garbage on return.
@@ -197,8 +198,7 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
  *   value_dtype          any of the same six (ignored for a keys-only sort).
  *   end_bit              a multiple of 8 in [8, key bits] (else SCAN_EINVAL);
  *                        end_bit / 8 digit passes.
- *   n                    0 <= n < 2^30 (else SCAN_EINVAL: the per-tile digit
- *                        counts travel in 30-bit words).
+ *   n                    0 <= n <= INT32_MAX.
  *   scratch              >= radix_sort_scratch_bytes(n, key_dtype) bytes,
  *                        16-byte aligned; needs no initialization.
  * No two of keys, tmp_keys, values, tmp_values and scratch may overlap.

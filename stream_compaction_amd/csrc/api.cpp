@@ -52,7 +52,6 @@ scan_status hip_status(hipError_t e) {
 }
 
 constexpr int64_t kMaxN = 2147483647;  // INT32_MAX
-constexpr int64_t kMaxSortN = int64_t(1) << 30;   // radix-sort counts are 30-bit
 
 }  // namespace
 
@@ -216,7 +215,7 @@ scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_value
     if (!fmt_of(value_dtype, &vf, &veb) || veb < 4) return SCAN_ENOTSUP;
     if (values == nullptr || tmp_values == nullptr) return SCAN_EINVAL;
   }
-  if (n < 0 || n >= kMaxSortN) return SCAN_EINVAL;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
   if (end_bit < 8 || end_bit > (int)(8 * keb) || end_bit % 8 != 0) return SCAN_EINVAL;
   if (n <= 1) return SCAN_OK;
   if (keys == nullptr || tmp_keys == nullptr || scratch == nullptr) return SCAN_EINVAL;
