@@ -229,6 +229,44 @@ scan_status select_compact(const void* in, const uint8_t* flags, void* out, int3
                            int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
                            void* stream);
 
+/*
+ * Device-count variants, for graph capture ("Algorithms" page, sections "Key
+ * sizing parameters" and "Capacity (log256_max_n)": the live count is read on
+ * the device and a fixed capacity sizes everything, so one captured graph
+ * replays across every count up to that capacity).  Each *_devn entry point
+ * does exactly what its namesake does, on n = n_live[0] elements, where that
+ * count is read by the kernels when they run and clamped to [0, capacity].
+ *   n_live     device pointer to one int32, 4-byte aligned; it must not
+ *              overlap anything the call writes.  NULL: SCAN_EINVAL.
+ *   capacity   takes the place of n in host-side validation, in the
+ *              *_scratch_bytes sizing and in the launch sizes (the grids
+ *              cover the capacity; work past the live count exits at once).
+ * Outputs past the live count are left untouched, as past n.
+ * radix_sort_devn needs an even number of digit passes (end_bit / 8 even,
+ * as the page requires of its sort) so that the result lands in keys
+ * without a copy sized on the host; otherwise SCAN_EINVAL.
+ */
+scan_status scan_device_devn(const void* in, void* out, const int32_t* n_live, int64_t capacity,
+                             scan_dtype dtype, scan_op op, void* scratch, size_t scratch_bytes,
+                             void* stream);
+scan_status scan_device_inclusive_devn(const void* in, void* out, const int32_t* n_live,
+                                       int64_t capacity, scan_dtype dtype, scan_op op,
+                                       void* scratch, size_t scratch_bytes, void* stream);
+scan_status reduce_device_devn(const void* in, void* out, const int32_t* n_live, int64_t capacity,
+                               scan_dtype dtype, scan_op op, void* scratch, size_t scratch_bytes,
+                               void* stream);
+scan_status reduce_by_key_devn(const void* keys_in, const void* values_in, void* keys_out,
+                               void* values_out, int32_t* num_runs, const int32_t* n_live,
+                               int64_t capacity, scan_dtype key_dtype, scan_dtype value_dtype,
+                               void* scratch, size_t scratch_bytes, void* stream);
+scan_status radix_sort_devn(void* keys, void* tmp_keys, void* values, void* tmp_values,
+                            const int32_t* n_live, int64_t capacity, scan_dtype key_dtype,
+                            scan_dtype value_dtype, int end_bit, void* scratch,
+                            size_t scratch_bytes, void* stream);
+scan_status select_compact_devn(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                                const int32_t* n_live, int64_t capacity, size_t elem_bytes,
+                                void* scratch, size_t scratch_bytes, void* stream);
+
 /* Static string naming a status code (never NULL). */
 const char* scan_status_str(scan_status s);
 

@@ -24,6 +24,10 @@ Entry points (same names as the C ABI):
   place, carrying values along.
 * ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
   stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
+* ``*_devn`` variants of the device-wide calls (C ABI names; ``n_live`` a
+  1-element int32 GPU tensor, ``capacity`` the tensors' length): the count is
+  read on the device, so one captured graph serves every count up to the
+  capacity.  Python wrappers: ``scan_device(..., n_live=t)`` and likewise.
 * ``scan_device_scratch_bytes(n, dtype)``, ``reduce_device_scratch_bytes(n,
   dtype)``, ``reduce_by_key_scratch_bytes(n)``, ``select_compact_scratch_bytes(n)``.
 """
@@ -41,8 +45,9 @@ OP_CODES = {"add": 1, "min": 2, "max": 3, "mul": 4}
 EXPORTS = ("scan_rows", "scan_device", "scan_device_inclusive", "scan_device_scratch_bytes",
            "reduce_device", "reduce_device_scratch_bytes", "reduce_by_key",
            "reduce_by_key_scratch_bytes", "radix_sort", "radix_sort_scratch_bytes",
-           "select_compact", "select_compact_scratch_bytes", "scan_status_str",
-           "scan_last_hip_error")
+           "select_compact", "select_compact_scratch_bytes", "scan_device_devn",
+           "scan_device_inclusive_devn", "reduce_device_devn", "reduce_by_key_devn",
+           "radix_sort_devn", "select_compact_devn", "scan_status_str", "scan_last_hip_error")
 
 _lib = None
 
@@ -90,6 +95,15 @@ def load(path):
     L.select_compact_scratch_bytes.restype = sz
     L.select_compact.argtypes = [vp, vp, vp, vp, i64, sz, vp, sz, vp]
     L.select_compact.restype = i32
+    for name in ("scan_device_devn", "scan_device_inclusive_devn", "reduce_device_devn"):
+        getattr(L, name).argtypes = [vp, vp, vp, i64, i32, i32, vp, sz, vp]
+        getattr(L, name).restype = i32
+    L.reduce_by_key_devn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, vp, sz, vp]
+    L.reduce_by_key_devn.restype = i32
+    L.radix_sort_devn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    L.radix_sort_devn.restype = i32
+    L.select_compact_devn.argtypes = [vp, vp, vp, vp, vp, i64, sz, vp, sz, vp]
+    L.select_compact_devn.restype = i32
     L.scan_status_str.argtypes = [i32]
     L.scan_status_str.restype = ctypes.c_char_p
     L.scan_last_hip_error.argtypes = []
@@ -176,17 +190,31 @@ def scan_device_scratch_bytes(n, dtype):
     return int(lib().scan_device_scratch_bytes(int(n), DTYPE_CODES[name]))
 
 
-def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
-    """Device-wide exclusive scan of the 1-D tensor ``x``."""
-    return _scan_device(lib().scan_device, x, op, out, scratch, stream, dtype)
+def _live(n_live, device):
+    """The device count of a *_devn call: a 1-element int32 GPU tensor."""
+    torch = _torch()
+    if n_live.numel() != 1 or n_live.dtype != torch.int32 or n_live.device != device:
+        raise ValueError("n_live must be a 1-element int32 tensor on the data's device")
+    return _dev_ptr(n_live, "n_live")
 
 
-def scan_device_inclusive(x, op="add", out=None, scratch=None, stream=None, dtype=None):
-    """Device-wide inclusive scan of the 1-D tensor ``x``."""
-    return _scan_device(lib().scan_device_inclusive, x, op, out, scratch, stream, dtype)
+def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None, n_live=None):
+    """Device-wide exclusive scan of the 1-D tensor ``x`` (of its first ``n_live[0]``
+    elements when ``n_live`` is given: the count is then read on the device)."""
+    L = lib()
+    fn = L.scan_device if n_live is None else L.scan_device_devn
+    return _scan_device(fn, x, op, out, scratch, stream, dtype, n_live)
 
 
-def _scan_device(fn, x, op, out, scratch, stream, dtype):
+def scan_device_inclusive(x, op="add", out=None, scratch=None, stream=None, dtype=None,
+                          n_live=None):
+    """Device-wide inclusive scan of the 1-D tensor ``x`` (``n_live`` as for scan_device)."""
+    L = lib()
+    fn = L.scan_device_inclusive if n_live is None else L.scan_device_inclusive_devn
+    return _scan_device(fn, x, op, out, scratch, stream, dtype, n_live)
+
+
+def _scan_device(fn, x, op, out, scratch, stream, dtype, n_live):
     torch = _torch()
     if x.dim() != 1:
         raise ValueError("x must be 1-D")
@@ -199,7 +227,8 @@ def _scan_device(fn, x, op, out, scratch, stream, dtype):
     need = scan_device_scratch_bytes(n, name)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    check(fn(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name], OP_CODES[op],
+    count = (n,) if n_live is None else (_live(n_live, x.device), n)
+    check(fn(_dev_ptr(x, "x"), _dev_ptr(out, "out"), *count, DTYPE_CODES[name], OP_CODES[op],
              _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
     return out
 
@@ -209,8 +238,9 @@ def reduce_device_scratch_bytes(n, dtype):
     return int(lib().reduce_device_scratch_bytes(int(n), DTYPE_CODES[name]))
 
 
-def reduce_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
-    """Device-wide reduction of the 1-D tensor ``x`` into ``out`` (1 element, on the GPU)."""
+def reduce_device(x, op="add", out=None, scratch=None, stream=None, dtype=None, n_live=None):
+    """Device-wide reduction of the 1-D tensor ``x`` into ``out`` (1 element, on the GPU);
+    ``n_live`` as for scan_device."""
     torch = _torch()
     if x.dim() != 1:
         raise ValueError("x must be 1-D")
@@ -223,9 +253,11 @@ def reduce_device(x, op="add", out=None, scratch=None, stream=None, dtype=None):
     need = reduce_device_scratch_bytes(n, name)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    check(lib().reduce_device(_dev_ptr(x, "x"), _dev_ptr(out, "out"), n, DTYPE_CODES[name],
-                              OP_CODES[op], _dev_ptr(scratch, "scratch"), scratch.numel(),
-                              _stream(stream)))
+    L = lib()
+    fn = L.reduce_device if n_live is None else L.reduce_device_devn
+    count = (n,) if n_live is None else (_live(n_live, x.device), n)
+    check(fn(_dev_ptr(x, "x"), _dev_ptr(out, "out"), *count, DTYPE_CODES[name], OP_CODES[op],
+             _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
     return out
 
 
@@ -234,7 +266,7 @@ def reduce_by_key_scratch_bytes(n):
 
 
 def reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None, scratch=None,
-                  stream=None, key_dtype=None, value_dtype=None):
+                  stream=None, key_dtype=None, value_dtype=None, n_live=None):
     """Collapse runs of equal consecutive keys of the 1-D ``keys`` into (first key, sum of
     ``values``).  Returns ``(keys_out, values_out, num_runs)``; ``num_runs`` is a 1-element
     int32 GPU tensor and only the first ``num_runs`` entries of the outputs are written."""
@@ -255,10 +287,13 @@ def reduce_by_key(keys, values, keys_out=None, values_out=None, num_runs=None, s
     need = reduce_by_key_scratch_bytes(n)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=keys.device)
-    check(lib().reduce_by_key(_dev_ptr(keys, "keys"), _dev_ptr(values, "values"),
-                              _dev_ptr(keys_out, "keys_out"), _dev_ptr(values_out, "values_out"),
-                              _dev_ptr(num_runs, "num_runs"), n, DTYPE_CODES[kd], DTYPE_CODES[vd],
-                              _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
+    L = lib()
+    fn = L.reduce_by_key if n_live is None else L.reduce_by_key_devn
+    count = (n,) if n_live is None else (_live(n_live, keys.device), n)
+    check(fn(_dev_ptr(keys, "keys"), _dev_ptr(values, "values"), _dev_ptr(keys_out, "keys_out"),
+             _dev_ptr(values_out, "values_out"), _dev_ptr(num_runs, "num_runs"), *count,
+             DTYPE_CODES[kd], DTYPE_CODES[vd], _dev_ptr(scratch, "scratch"), scratch.numel(),
+             _stream(stream)))
     return keys_out, values_out, num_runs
 
 
@@ -268,7 +303,7 @@ def radix_sort_scratch_bytes(n, key_dtype):
 
 
 def radix_sort(keys, values=None, tmp_keys=None, tmp_values=None, end_bit=None, scratch=None,
-               stream=None, key_dtype=None, value_dtype=None):
+               stream=None, key_dtype=None, value_dtype=None, n_live=None):
     """Stable ascending radix sort of the 1-D ``keys`` in place (``values`` in place
     alongside).  Returns ``(keys, values)``."""
     torch = _torch()
@@ -292,9 +327,12 @@ def radix_sort(keys, values=None, tmp_keys=None, tmp_values=None, end_bit=None, 
     need = radix_sort_scratch_bytes(n, kd)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=keys.device)
-    check(lib().radix_sort(_dev_ptr(keys, "keys"), _dev_ptr(tmp_keys, "tmp_keys"), vptr, tvptr, n,
-                           DTYPE_CODES[kd], vd, int(end_bit), _dev_ptr(scratch, "scratch"),
-                           scratch.numel(), _stream(stream)))
+    L = lib()
+    fn = L.radix_sort if n_live is None else L.radix_sort_devn
+    count = (n,) if n_live is None else (_live(n_live, keys.device), n)
+    check(fn(_dev_ptr(keys, "keys"), _dev_ptr(tmp_keys, "tmp_keys"), vptr, tvptr, *count,
+             DTYPE_CODES[kd], vd, int(end_bit), _dev_ptr(scratch, "scratch"), scratch.numel(),
+             _stream(stream)))
     return keys, values
 
 
@@ -302,7 +340,7 @@ def select_compact_scratch_bytes(n):
     return int(lib().select_compact_scratch_bytes(int(n)))
 
 
-def select_compact(x, flags, out=None, num_out=None, scratch=None, stream=None):
+def select_compact(x, flags, out=None, num_out=None, scratch=None, stream=None, n_live=None):
     """Stable compaction of the 1-D tensor ``x`` by nonzero uint8 ``flags``.
 
     Returns ``(out, num_out)``; ``num_out`` is a 1-element int32 GPU tensor
@@ -323,7 +361,10 @@ def select_compact(x, flags, out=None, num_out=None, scratch=None, stream=None):
     need = select_compact_scratch_bytes(n)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    check(lib().select_compact(_dev_ptr(x, "x"), _dev_ptr(flags, "flags"), _dev_ptr(out, "out"),
-                               _dev_ptr(num_out, "num_out"), n, x.element_size(),
-                               _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
+    L = lib()
+    fn = L.select_compact if n_live is None else L.select_compact_devn
+    count = (n,) if n_live is None else (_live(n_live, x.device), n)
+    check(fn(_dev_ptr(x, "x"), _dev_ptr(flags, "flags"), _dev_ptr(out, "out"),
+             _dev_ptr(num_out, "num_out"), *count, x.element_size(),
+             _dev_ptr(scratch, "scratch"), scratch.numel(), _stream(stream)))
     return out, num_out

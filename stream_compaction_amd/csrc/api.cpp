@@ -45,6 +45,17 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t round16(size_t b) { return (b + 15) & ~(size_t)15; }
 
+// The device count of the *_devn entry points: present, 4-byte aligned and
+// outside every range the call writes (each workgroup reads it once, so the
+// call must not change it).
+scan_status devn_check(const int32_t* n_dev, const void* const* written, const size_t* sizes,
+                       int count) {
+  if (n_dev == nullptr || !aligned(n_dev, 4)) return SCAN_EINVAL;
+  for (int i = 0; i < count; ++i)
+    if (overlap(n_dev, 4, written[i], sizes[i])) return SCAN_EALIAS;
+  return SCAN_OK;
+}
+
 scan_status hip_status(hipError_t e) {
   if (e == hipSuccess) return SCAN_OK;
   g_last_hip_error = (int)e;
@@ -99,7 +110,8 @@ size_t scan_device_scratch_bytes(int64_t n, scan_dtype dtype) {
 
 static scan_status scan_device_any(const void* in, void* out, int64_t n, scan_dtype dtype,
                                    scan_op op, bool inclusive, void* scratch,
-                                   size_t scratch_bytes, void* stream) {
+                                   size_t scratch_bytes, void* stream, bool devn,
+                                   const int32_t* n_dev) {
   sca::Fmt fmt;
   size_t eb;
   if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
@@ -115,19 +127,43 @@ static scan_status scan_device_any(const void* in, void* out, int64_t n, scan_dt
   const size_t bytes = (size_t)n * eb;
   if (overlap(in, bytes, out, bytes)) return SCAN_EALIAS;
   if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes)) return SCAN_EALIAS;
-  return hip_status(
-      sca::launch_scan_device(in, out, n, fmt, opi, inclusive, scratch, (hipStream_t)stream));
+  if (devn) {
+    const void* w[2] = {out, scratch};
+    const size_t z[2] = {bytes, need};
+    const scan_status dv = devn_check(n_dev, w, z, 2);
+    if (dv != SCAN_OK) return dv;
+  }
+  return hip_status(sca::launch_scan_device(in, out, n, fmt, opi, inclusive, scratch,
+                                            (hipStream_t)stream, n_dev));
 }
 
 scan_status scan_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
                         void* scratch, size_t scratch_bytes, void* stream) {
-  return scan_device_any(in, out, n, dtype, op, false, scratch, scratch_bytes, stream);
+  return scan_device_any(in, out, n, dtype, op, false, scratch, scratch_bytes, stream, false,
+                         nullptr);
+}
+
+scan_status scan_device_devn(const void* in, void* out, const int32_t* n_live, int64_t capacity,
+                             scan_dtype dtype, scan_op op, void* scratch, size_t scratch_bytes,
+                             void* stream) {
+  if (n_live == nullptr) return SCAN_EINVAL;
+  return scan_device_any(in, out, capacity, dtype, op, false, scratch, scratch_bytes, stream, true,
+                         n_live);
 }
 
 scan_status scan_device_inclusive(const void* in, void* out, int64_t n, scan_dtype dtype,
                                   scan_op op, void* scratch, size_t scratch_bytes,
                                   void* stream) {
-  return scan_device_any(in, out, n, dtype, op, true, scratch, scratch_bytes, stream);
+  return scan_device_any(in, out, n, dtype, op, true, scratch, scratch_bytes, stream, false,
+                         nullptr);
+}
+
+scan_status scan_device_inclusive_devn(const void* in, void* out, const int32_t* n_live,
+                                       int64_t capacity, scan_dtype dtype, scan_op op,
+                                       void* scratch, size_t scratch_bytes, void* stream) {
+  if (n_live == nullptr) return SCAN_EINVAL;
+  return scan_device_any(in, out, capacity, dtype, op, true, scratch, scratch_bytes, stream, true,
+                         n_live);
 }
 
 size_t reduce_device_scratch_bytes(int64_t n, scan_dtype dtype) {
@@ -137,8 +173,9 @@ size_t reduce_device_scratch_bytes(int64_t n, scan_dtype dtype) {
   return round16(sca::reduce_partials(n, fmt) * 8);
 }
 
-scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
-                          void* scratch, size_t scratch_bytes, void* stream) {
+static scan_status reduce_any(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                              void* scratch, size_t scratch_bytes, void* stream, bool devn,
+                              const int32_t* n_dev) {
   sca::Fmt fmt;
   size_t eb;
   if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
@@ -156,7 +193,26 @@ scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype
     if (overlap(in, bytes, out, eb)) return SCAN_EALIAS;
     if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, eb)) return SCAN_EALIAS;
   }
-  return hip_status(sca::launch_reduce(in, out, n, fmt, opi, scratch, (hipStream_t)stream));
+  if (devn) {
+    const void* w[2] = {out, scratch};
+    const size_t z[2] = {eb, n > 0 ? need : 0};
+    const scan_status dv = devn_check(n_dev, w, z, 2);
+    if (dv != SCAN_OK) return dv;
+  }
+  return hip_status(
+      sca::launch_reduce(in, out, n, fmt, opi, scratch, (hipStream_t)stream, n_dev));
+}
+
+scan_status reduce_device(const void* in, void* out, int64_t n, scan_dtype dtype, scan_op op,
+                          void* scratch, size_t scratch_bytes, void* stream) {
+  return reduce_any(in, out, n, dtype, op, scratch, scratch_bytes, stream, false, nullptr);
+}
+
+scan_status reduce_device_devn(const void* in, void* out, const int32_t* n_live, int64_t capacity,
+                               scan_dtype dtype, scan_op op, void* scratch, size_t scratch_bytes,
+                               void* stream) {
+  if (n_live == nullptr) return SCAN_EINVAL;
+  return reduce_any(in, out, capacity, dtype, op, scratch, scratch_bytes, stream, true, n_live);
 }
 
 size_t reduce_by_key_scratch_bytes(int64_t n) {
@@ -164,10 +220,10 @@ size_t reduce_by_key_scratch_bytes(int64_t n) {
   return sca::desc_scratch_bytes(sca::reduce_by_key_tiles(n));
 }
 
-scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys_out,
-                          void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
-                          scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
-                          void* stream) {
+static scan_status rbk_any(const void* keys_in, const void* values_in, void* keys_out,
+                           void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
+                           scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
+                           void* stream, bool devn, const int32_t* n_dev) {
   sca::Fmt kf, vf;
   size_t keb, veb;
   if (!fmt_of(key_dtype, &kf, &keb) || !fmt_of(value_dtype, &vf, &veb)) return SCAN_ENOTSUP;
@@ -194,8 +250,32 @@ scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys
       for (int b = a + 1; b < 6; ++b)
         if (!(a == 0 && b == 1) && overlap(r[a], z[a], r[b], z[b])) return SCAN_EALIAS;
   }
+  if (devn) {
+    const size_t bytes = (size_t)n * 4;
+    const void* w[4] = {keys_out, values_out, num_runs, scratch};
+    const size_t z[4] = {bytes, bytes, 4, n > 0 ? reduce_by_key_scratch_bytes(n) : 0};
+    const scan_status dv = devn_check(n_dev, w, z, 4);
+    if (dv != SCAN_OK) return dv;
+  }
   return hip_status(sca::launch_reduce_by_key(keys_in, values_in, keys_out, values_out, num_runs,
-                                              n, kf, vf, scratch, (hipStream_t)stream));
+                                              n, kf, vf, scratch, (hipStream_t)stream, n_dev));
+}
+
+scan_status reduce_by_key(const void* keys_in, const void* values_in, void* keys_out,
+                          void* values_out, int32_t* num_runs, int64_t n, scan_dtype key_dtype,
+                          scan_dtype value_dtype, void* scratch, size_t scratch_bytes,
+                          void* stream) {
+  return rbk_any(keys_in, values_in, keys_out, values_out, num_runs, n, key_dtype, value_dtype,
+                 scratch, scratch_bytes, stream, false, nullptr);
+}
+
+scan_status reduce_by_key_devn(const void* keys_in, const void* values_in, void* keys_out,
+                               void* values_out, int32_t* num_runs, const int32_t* n_live,
+                               int64_t capacity, scan_dtype key_dtype, scan_dtype value_dtype,
+                               void* scratch, size_t scratch_bytes, void* stream) {
+  if (n_live == nullptr) return SCAN_EINVAL;
+  return rbk_any(keys_in, values_in, keys_out, values_out, num_runs, capacity, key_dtype,
+                 value_dtype, scratch, scratch_bytes, stream, true, n_live);
 }
 
 size_t radix_sort_scratch_bytes(int64_t n, scan_dtype key_dtype) {
@@ -205,9 +285,10 @@ size_t radix_sort_scratch_bytes(int64_t n, scan_dtype key_dtype) {
   return round16(sca::radix_sort_scratch(n, eb));
 }
 
-scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
-                       scan_dtype key_dtype, scan_dtype value_dtype, int end_bit, void* scratch,
-                       size_t scratch_bytes, void* stream) {
+static scan_status sort_any(void* keys, void* tmp_keys, void* values, void* tmp_values,
+                            int64_t n, scan_dtype key_dtype, scan_dtype value_dtype, int end_bit,
+                            void* scratch, size_t scratch_bytes, void* stream, bool devn,
+                            const int32_t* n_dev) {
   sca::Fmt kf, vf;
   size_t keb, veb = 0;
   if (!fmt_of(key_dtype, &kf, &keb) || keb < 4) return SCAN_ENOTSUP;
@@ -217,6 +298,8 @@ scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_value
   }
   if (n < 0 || n > kMaxN) return SCAN_EINVAL;
   if (end_bit < 8 || end_bit > (int)(8 * keb) || end_bit % 8 != 0) return SCAN_EINVAL;
+  if (devn && (end_bit / 8) % 2 != 0) return SCAN_EINVAL;   // the result must land in keys
+  if (devn && n_dev == nullptr) return SCAN_EINVAL;
   if (n <= 1) return SCAN_OK;
   if (keys == nullptr || tmp_keys == nullptr || scratch == nullptr) return SCAN_EINVAL;
   if (!aligned(keys, keb) || !aligned(tmp_keys, keb) || !aligned(scratch, 16)) return SCAN_EINVAL;
@@ -229,8 +312,27 @@ scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_value
   for (int a = 0; a < 5; ++a)
     for (int b = a + 1; b < 5; ++b)
       if (overlap(r[a], z[a], r[b], z[b])) return SCAN_EALIAS;
+  if (devn) {
+    const scan_status dv = devn_check(n_dev, r, z, 5);
+    if (dv != SCAN_OK) return dv;
+  }
   return hip_status(sca::launch_radix_sort(keys, tmp_keys, values, tmp_values, n, kf, (int)veb,
-                                           end_bit, scratch, (hipStream_t)stream));
+                                           end_bit, scratch, (hipStream_t)stream, n_dev));
+}
+
+scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
+                       scan_dtype key_dtype, scan_dtype value_dtype, int end_bit, void* scratch,
+                       size_t scratch_bytes, void* stream) {
+  return sort_any(keys, tmp_keys, values, tmp_values, n, key_dtype, value_dtype, end_bit, scratch,
+                  scratch_bytes, stream, false, nullptr);
+}
+
+scan_status radix_sort_devn(void* keys, void* tmp_keys, void* values, void* tmp_values,
+                            const int32_t* n_live, int64_t capacity, scan_dtype key_dtype,
+                            scan_dtype value_dtype, int end_bit, void* scratch,
+                            size_t scratch_bytes, void* stream) {
+  return sort_any(keys, tmp_keys, values, tmp_values, capacity, key_dtype, value_dtype, end_bit,
+                  scratch, scratch_bytes, stream, true, n_live);
 }
 
 size_t select_compact_scratch_bytes(int64_t n) {
@@ -238,9 +340,9 @@ size_t select_compact_scratch_bytes(int64_t n) {
   return sca::desc_scratch_bytes(sca::select_tiles(n, 8));
 }
 
-scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                           int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
-                           void* stream) {
+static scan_status select_any(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                              int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
+                              void* stream, bool devn, const int32_t* n_dev) {
   if (elem_bytes != 4 && elem_bytes != 8) return SCAN_ENOTSUP;
   if (n < 0 || n > kMaxN) return SCAN_EINVAL;
   if (num_out == nullptr || !aligned(num_out, 4)) return SCAN_EINVAL;
@@ -261,8 +363,29 @@ scan_status select_compact(const void* in, const uint8_t* flags, void* out, int3
     for (int a = 0; a < 4; ++a)
       if (overlap(out, bytes, ranges[a], sizes[a])) return SCAN_EALIAS;
   }
+  if (devn) {
+    const void* w[3] = {out, num_out, scratch};
+    const size_t z[3] = {(size_t)n * elem_bytes, 4, n > 0 ? select_compact_scratch_bytes(n) : 0};
+    const scan_status dv = devn_check(n_dev, w, z, 3);
+    if (dv != SCAN_OK) return dv;
+  }
   return hip_status(sca::launch_select(in, flags, out, num_out, n, elem_bytes, scratch,
-                                       (hipStream_t)stream));
+                                       (hipStream_t)stream, n_dev));
+}
+
+scan_status select_compact(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                           int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
+                           void* stream) {
+  return select_any(in, flags, out, num_out, n, elem_bytes, scratch, scratch_bytes, stream, false,
+                    nullptr);
+}
+
+scan_status select_compact_devn(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
+                                const int32_t* n_live, int64_t capacity, size_t elem_bytes,
+                                void* scratch, size_t scratch_bytes, void* stream) {
+  if (n_live == nullptr) return SCAN_EINVAL;
+  return select_any(in, flags, out, num_out, capacity, elem_bytes, scratch, scratch_bytes, stream,
+                    true, n_live);
 }
 
 }  // extern "C"

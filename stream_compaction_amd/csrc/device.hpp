@@ -531,6 +531,16 @@ __device__ __forceinline__ W look_back(const uint64_t* desc, int64_t tile, uint6
   }
 }
 
+// The live element count of a call: n_cap, or, when the caller keeps the
+// count in device memory (the entry points that take a device count, so one
+// captured graph serves every count up to a capacity), that count clamped to
+// [0, n_cap].  Read once per wave; the same value in every lane.
+__device__ __forceinline__ int64_t live_count(int64_t n_cap, const int32_t* n_dev) {
+  if (n_dev == nullptr) return n_cap;
+  const int64_t v = *n_dev;
+  return v < 0 ? 0 : (v > n_cap ? n_cap : v);
+}
+
 // Wait bound of the look-back before it reduces a late predecessor itself,
 // in ticks of the 100 MHz real-time counter.  Far above the latency of a
 // published descriptor (microseconds), so in practice it only matters if a

@@ -20,32 +20,38 @@ hipError_t launch_scan_rows(const void* in, void* out, int64_t rows, int64_t n, 
 
 // Device-wide exclusive (or inclusive) scan; op: 0 add, 1 min, 2 max.
 size_t scan_device_tiles(int64_t n, Fmt fmt);       // descriptors needed
+// n_dev (all launchers below): when not null, the live count is read from it
+// on the device and clamped to [0, n]; n is then the capacity that grids and
+// scratch are sized for.
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
-                              bool inclusive, void* scratch, hipStream_t stream);
+                              bool inclusive, void* scratch, hipStream_t stream,
+                              const int32_t* n_dev = nullptr);
 
 // Device-wide reduction into out[0]; op: 0 add, 1 min, 2 max.  n == 0 writes
 // the identity.  Scratch holds one partial per workgroup of the first launch.
 size_t reduce_partials(int64_t n, Fmt fmt);         // partials (8-byte slots) needed
 hipError_t launch_reduce(const void* in, void* out, int64_t n, Fmt fmt, int op, void* scratch,
-                         hipStream_t stream);
+                         hipStream_t stream, const int32_t* n_dev = nullptr);
 
 // Reduce-by-key (32-bit keys and values): one descriptor (four 64-bit words)
 // per tile.
 size_t reduce_by_key_tiles(int64_t n);
 hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys_out,
                                 void* values_out, int32_t* num_runs, int64_t n, Fmt kfmt,
-                                Fmt vfmt, void* scratch, hipStream_t stream);
+                                Fmt vfmt, void* scratch, hipStream_t stream,
+                                const int32_t* n_dev = nullptr);
 
 // Radix sort (n < 2^30); value_bytes 0 (keys only), 4 or 8.
 size_t radix_sort_scratch(int64_t n, size_t key_bytes);
 hipError_t launch_radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
                              Fmt kfmt, int value_bytes, int end_bit, void* scratch,
-                             hipStream_t stream);
+                             hipStream_t stream, const int32_t* n_dev = nullptr);
 
 // Stream compaction.
 size_t select_tiles(int64_t n, size_t elem_bytes);
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                         int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream);
+                         int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream,
+                         const int32_t* n_dev = nullptr);
 
 // Scratch of the look-back kernels holds only the tile descriptors, one per
 // 128-byte line (kDescBytes), whose used words are zeroed at the start of

@@ -57,7 +57,8 @@ constexpr int kRxBins = 256;
 // ---------------------------------------------------------------------------
 template <class KT, KeyKind KK, int WAVES, int KPT>
 __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
-    const KT* __restrict__ kin, int64_t n, int shift, int64_t ntiles, uint32_t* hist) {
+    const KT* __restrict__ kin, int64_t n_cap, const int32_t* n_dev, int shift, int64_t ntiles,
+    uint32_t* hist) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
   static_assert(kThreads >= kRxBins, "one thread per digit");
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
   const int tid = threadIdx.x, wave = wave_id();
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTile;
-  const int count = (int)((n - t0) < kTile ? (n - t0) : kTile);
+  const int64_t n = live_count(n_cap, n_dev);
+  const int count = (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
   for (int i = tid; i < WAVES * kRxBins; i += kThreads) (&s_h[0][0])[i] = 0u;
   __syncthreads();
   // 16-byte loads through a buffer resource bounded at the tile's last key
@@ -113,7 +115,7 @@ template <> struct ValBits<8> { using T = uint64_t; };
 template <class KT, KeyKind KK, int VB, int WAVES, int KPT>
 __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
-    void* __restrict__ vout_, int64_t n, int shift, int64_t ntiles,
+    void* __restrict__ vout_, int64_t n_cap, const int32_t* n_dev, int shift, int64_t ntiles,
     const uint32_t* __restrict__ offsets) {
   using VT = typename ValBits<VB>::T;
   constexpr int kThreads = 64 * WAVES;
@@ -133,7 +135,9 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTile;
-  const int count = (int)((n - t0) < kTile ? (n - t0) : kTile);   // keys in this tile
+  const int64_t n = live_count(n_cap, n_dev);
+  const int count =                                  // keys in this tile
+      (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
   for (int i = tid; i < WAVES * kRxBins; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
   if (tid < kRxBins) s_g[tid] = offsets[(int64_t)tid * ntiles + tile];
   __syncthreads();
@@ -306,9 +310,13 @@ size_t radix_sort_scratch(int64_t n, size_t key_bytes) {
 
 template <class KT, KeyKind KK, int VB>
 static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
-                              int end_bit, void* scratch, hipStream_t stream) {
+                              int end_bit, void* scratch, hipStream_t stream,
+                              const int32_t* n_dev) {
   constexpr int W = RxShape<KT>::kWaves, KPT = RxShape<KT>::kKpt;
   const int npass = end_bit / 8;
+  // with a device count the result must land in `keys` by itself (an even
+  // number of passes): a copy back would need the count on the host
+  if (n_dev != nullptr && npass % 2 == 1) return hipErrorInvalidValue;
   const int64_t ntiles = rx_ntiles(n, sizeof(KT));
   uint32_t* hist = (uint32_t*)scratch;
   uint32_t* offs = (uint32_t*)((char*)scratch + rx_hist_bytes(ntiles));
@@ -320,14 +328,14 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
   hipError_t err = hipSuccess;
   for (int p = 0; p < npass; ++p) {
     radix_tile_hist_kernel<KT, KK, W, KPT><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
-        src, n, 8 * p, ntiles, hist);
+        src, n, n_dev, 8 * p, ntiles, hist);
     err = hipGetLastError();
     if (err == hipSuccess)
       err = launch_scan_device(hist, offs, ntiles * kRxBins, Fmt::U32, 0, false, scan_scratch,
                                stream);
     if (err != hipSuccess) return err;
     radix_scatter_kernel<KT, KK, VB, W, KPT><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
-        src, dst, vsrc, vdst, n, 8 * p, ntiles, offs);
+        src, dst, vsrc, vdst, n, n_dev, 8 * p, ntiles, offs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     KT* ts = src; src = dst; dst = ts;
@@ -342,25 +350,26 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
 
 template <class KT, KeyKind KK>
 static hipError_t launch_rx_v(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
-                              int value_bytes, int end_bit, void* scratch, hipStream_t stream) {
+                              int value_bytes, int end_bit, void* scratch, hipStream_t stream,
+                              const int32_t* n_dev) {
   switch (value_bytes) {
-    case 0: return launch_rx_t<KT, KK, 0>(keys, tmp_keys, nullptr, nullptr, n, end_bit, scratch, stream);
-    case 4: return launch_rx_t<KT, KK, 4>(keys, tmp_keys, values, tmp_values, n, end_bit, scratch, stream);
-    default: return launch_rx_t<KT, KK, 8>(keys, tmp_keys, values, tmp_values, n, end_bit, scratch, stream);
+    case 0: return launch_rx_t<KT, KK, 0>(keys, tmp_keys, nullptr, nullptr, n, end_bit, scratch, stream, n_dev);
+    case 4: return launch_rx_t<KT, KK, 4>(keys, tmp_keys, values, tmp_values, n, end_bit, scratch, stream, n_dev);
+    default: return launch_rx_t<KT, KK, 8>(keys, tmp_keys, values, tmp_values, n, end_bit, scratch, stream, n_dev);
   }
 }
 
 hipError_t launch_radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
                              Fmt kfmt, int value_bytes, int end_bit, void* scratch,
-                             hipStream_t stream) {
+                             hipStream_t stream, const int32_t* n_dev) {
   if (n <= 1) return hipSuccess;
   switch (kfmt) {
-    case Fmt::U32: return launch_rx_v<uint32_t, KeyKind::Unsigned>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
-    case Fmt::I32: return launch_rx_v<uint32_t, KeyKind::Signed>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
-    case Fmt::F32: return launch_rx_v<uint32_t, KeyKind::Float>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
-    case Fmt::U64: return launch_rx_v<uint64_t, KeyKind::Unsigned>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
-    case Fmt::I64: return launch_rx_v<uint64_t, KeyKind::Signed>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
-    case Fmt::F64: return launch_rx_v<uint64_t, KeyKind::Float>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream);
+    case Fmt::U32: return launch_rx_v<uint32_t, KeyKind::Unsigned>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
+    case Fmt::I32: return launch_rx_v<uint32_t, KeyKind::Signed>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
+    case Fmt::F32: return launch_rx_v<uint32_t, KeyKind::Float>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
+    case Fmt::U64: return launch_rx_v<uint64_t, KeyKind::Unsigned>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
+    case Fmt::I64: return launch_rx_v<uint64_t, KeyKind::Signed>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
+    case Fmt::F64: return launch_rx_v<uint64_t, KeyKind::Float>(keys, tmp_keys, values, tmp_values, n, value_bytes, end_bit, scratch, stream, n_dev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -37,7 +37,7 @@ constexpr int64_t kRedMaxBlocks = 2048;
 
 template <class F, Op O, int E>
 __global__ __launch_bounds__(64 * kRedWaves) void reduce_partials_kernel(
-    uintptr_t in_base, int64_t n, int64_t ph, int64_t runs, int64_t runs_per_wave,
+    uintptr_t in_base, int64_t n_cap, const int32_t* n_dev, int64_t ph, int64_t runs_per_wave,
     uintptr_t partials) {
   using S = typename F::S;
   using W = typename F::W;
@@ -49,7 +49,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void reduce_partials_kernel(
 
   const int lane = lane_id(), wave = wave_id();
   const W id = identity<O, W>();
+  const int64_t n = live_count(n_cap, n_dev);
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  const int64_t runs = n == 0 ? 0 : v_last / kRedRunVecs + 1;   // runs holding live elements
   const int64_t gw = (int64_t)blockIdx.x * kRedWaves + wave;
   const int64_t r0 = gw * runs_per_wave;
   const int64_t r1 = (r0 + runs_per_wave < runs) ? r0 + runs_per_wave : runs;
@@ -149,7 +151,7 @@ size_t reduce_partials(int64_t n, Fmt fmt) {
 
 template <class F, Op O>
 static hipError_t launch_red_t(const void* in, void* out, int64_t n, void* scratch,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t* n_dev) {
   using S = typename F::S;
   constexpr int EV = 16 / (int)sizeof(S);
   const uintptr_t ia = (uintptr_t)in;
@@ -157,7 +159,7 @@ static hipError_t launch_red_t(const void* in, void* out, int64_t n, void* scrat
   const RedGeom g = red_geom(n, EV, ph);
   if (g.blocks > 0) {
     reduce_partials_kernel<F, O, EV><<<dim3((unsigned)g.blocks), dim3(64 * kRedWaves), 0, stream>>>(
-        ia - (uintptr_t)ph * sizeof(S), n, ph, g.runs, g.runs_per_wave, (uintptr_t)scratch);
+        ia - (uintptr_t)ph * sizeof(S), n, n_dev, ph, g.runs_per_wave, (uintptr_t)scratch);
   }
   reduce_final_kernel<F, O><<<dim3(1), dim3(64), 0, stream>>>((uintptr_t)scratch, g.blocks,
                                                              (uintptr_t)out);
@@ -166,23 +168,23 @@ static hipError_t launch_red_t(const void* in, void* out, int64_t n, void* scrat
 
 template <class F>
 static hipError_t launch_red_f(const void* in, void* out, int64_t n, int op, void* scratch,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t* n_dev) {
   switch (op) {
-    case 0: return launch_red_t<F, Op::Add>(in, out, n, scratch, stream);
-    case 1: return launch_red_t<F, Op::Min>(in, out, n, scratch, stream);
-    default: return launch_red_t<F, Op::Max>(in, out, n, scratch, stream);
+    case 0: return launch_red_t<F, Op::Add>(in, out, n, scratch, stream, n_dev);
+    case 1: return launch_red_t<F, Op::Min>(in, out, n, scratch, stream, n_dev);
+    default: return launch_red_t<F, Op::Max>(in, out, n, scratch, stream, n_dev);
   }
 }
 
 hipError_t launch_reduce(const void* in, void* out, int64_t n, Fmt fmt, int op, void* scratch,
-                         hipStream_t stream) {
+                         hipStream_t stream, const int32_t* n_dev) {
   switch (fmt) {
-    case Fmt::I32: return launch_red_f<FmtI32>(in, out, n, op, scratch, stream);
-    case Fmt::U32: return launch_red_f<FmtU32>(in, out, n, op, scratch, stream);
-    case Fmt::F32: return launch_red_f<FmtF32>(in, out, n, op, scratch, stream);
-    case Fmt::I64: return launch_red_f<FmtI64>(in, out, n, op, scratch, stream);
-    case Fmt::U64: return launch_red_f<FmtU64>(in, out, n, op, scratch, stream);
-    case Fmt::F64: return launch_red_f<FmtF64>(in, out, n, op, scratch, stream);
+    case Fmt::I32: return launch_red_f<FmtI32>(in, out, n, op, scratch, stream, n_dev);
+    case Fmt::U32: return launch_red_f<FmtU32>(in, out, n, op, scratch, stream, n_dev);
+    case Fmt::F32: return launch_red_f<FmtF32>(in, out, n, op, scratch, stream, n_dev);
+    case Fmt::I64: return launch_red_f<FmtI64>(in, out, n, op, scratch, stream, n_dev);
+    case Fmt::U64: return launch_red_f<FmtU64>(in, out, n, op, scratch, stream, n_dev);
+    case Fmt::F64: return launch_red_f<FmtF64>(in, out, n, op, scratch, stream, n_dev);
     default: return hipErrorInvalidValue;
   }
 }

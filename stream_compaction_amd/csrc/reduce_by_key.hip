@@ -92,7 +92,7 @@ __device__ __forceinline__ uint32_t key_at(uintptr_t k_base, int64_t i, int64_t 
 
 template <class KF, class VF, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
-    uintptr_t k_base, uintptr_t v_base, int64_t n, int64_t ph, int64_t ntiles,
+    uintptr_t k_base, uintptr_t v_base, int64_t n_cap, const int32_t* n_dev, int64_t ph,
     uintptr_t keys_out, uintptr_t values_out, uintptr_t num_runs, uint64_t* desc) {
   using V = typename ValT<VF>::V;
   using W = Seg<V>;
@@ -110,7 +110,12 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const W id = W(0);
+  const int64_t n = live_count(n_cap, n_dev);
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  if (n == 0 || tile * kTileVecs > v_last) {         // past the live count: nothing to do
+    if (n == 0 && tile == 0 && threadIdx.x == 0) *gptr<int32_t>(num_runs) = 0;
+    return;
+  }
   if (threadIdx.x == 0) {
     s_posted = 0u;
     s_agg_done = 0u;
@@ -254,7 +259,7 @@ size_t reduce_by_key_tiles(int64_t n) { return (size_t)rbk_tiles_for(n, 1, kRbkM
 template <class KF, class VF, int WD, int K>
 static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* keys_out,
                                  void* values_out, int32_t* num_runs, int64_t n, void* scratch,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int32_t* n_dev) {
   constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ka = (uintptr_t)keys, va = (uintptr_t)values;
   const bool vec = (ka % 16) == (va % 16);
@@ -268,10 +273,10 @@ static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* key
   const uintptr_t ko = (uintptr_t)keys_out, vo = (uintptr_t)values_out, nr = (uintptr_t)num_runs;
   if (vec) {
     reduce_by_key_kernel<KF, VF, 4, WD, K><<<grid, block, 0, stream>>>(
-        ka - ph * 4, va - ph * 4, n, ph, ntiles, ko, vo, nr, desc);
+        ka - ph * 4, va - ph * 4, n, n_dev, ph, ko, vo, nr, desc);
   } else {
     reduce_by_key_kernel<KF, VF, 1, WD, K><<<grid, block, 0, stream>>>(
-        ka, va, n, 0, ntiles, ko, vo, nr, desc);
+        ka, va, n, n_dev, 0, ko, vo, nr, desc);
   }
   return hipGetLastError();
 }
@@ -279,28 +284,29 @@ static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* key
 template <class KF, class VF>
 static hipError_t launch_rbk_t(const void* keys, const void* values, void* keys_out,
                                void* values_out, int32_t* num_runs, int64_t n, void* scratch,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t* n_dev) {
   return launch_rbk_cfg<KF, VF, 7, 8>(keys, values, keys_out, values_out, num_runs, n, scratch,
-                                      stream);
+                                      stream, n_dev);
 }
 
 template <class KF>
 static hipError_t launch_rbk_k(const void* keys, const void* values, void* keys_out,
                                void* values_out, int32_t* num_runs, int64_t n, Fmt vfmt,
-                               void* scratch, hipStream_t stream) {
+                               void* scratch, hipStream_t stream, const int32_t* n_dev) {
   switch (vfmt) {
     case Fmt::F32:
       return launch_rbk_t<KF, FmtF32>(keys, values, keys_out, values_out, num_runs, n, scratch,
-                                      stream);
+                                      stream, n_dev);
     default:   // i32 and u32 values share the wrapping add
       return launch_rbk_t<KF, FmtU32>(keys, values, keys_out, values_out, num_runs, n, scratch,
-                                      stream);
+                                      stream, n_dev);
   }
 }
 
 hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys_out,
                                 void* values_out, int32_t* num_runs, int64_t n, Fmt kfmt,
-                                Fmt vfmt, void* scratch, hipStream_t stream) {
+                                Fmt vfmt, void* scratch, hipStream_t stream,
+                                const int32_t* n_dev) {
   if (n == 0) {
     rbk_count_zero_kernel<<<dim3(1), dim3(1), 0, stream>>>(num_runs);
     return hipGetLastError();
@@ -308,10 +314,10 @@ hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys
   switch (kfmt) {
     case Fmt::F32:
       return launch_rbk_k<FmtF32>(keys, values, keys_out, values_out, num_runs, n, vfmt, scratch,
-                                  stream);
+                                  stream, n_dev);
     default:   // i32 and u32 keys compare as bits
       return launch_rbk_k<FmtU32>(keys, values, keys_out, values_out, num_runs, n, vfmt, scratch,
-                                  stream);
+                                  stream, n_dev);
   }
 }
 

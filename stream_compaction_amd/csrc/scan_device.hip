@@ -37,7 +37,8 @@ constexpr int64_t kDevMinTileVecs = 7168;
 
 template <class F, Op O, bool INCL, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
-    uintptr_t in_base, uintptr_t out_base, int64_t n, int64_t ph, int64_t ntiles, uint64_t* desc) {
+    uintptr_t in_base, uintptr_t out_base, int64_t n_cap, const int32_t* n_dev, int64_t ph,
+    uint64_t* desc) {
   using S = typename F::S;
   using W = typename F::W;
   using IO = VecIO<S, E>;
@@ -53,7 +54,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
   const W id = identity<O, W>();
+  const int64_t n = live_count(n_cap, n_dev);
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  if (n == 0 || tile * kTileVecs > v_last) return;   // past the live count: nothing to do
   if (threadIdx.x == 0) {
     s_posted = 0u;
     s_agg_done = 0u;
@@ -180,7 +183,7 @@ size_t scan_device_tiles(int64_t n, Fmt fmt) {
 // lane per tile.
 template <class F, Op O, bool INCL, int WD, int K>
 static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int32_t* n_dev) {
   using S = typename F::S;
   constexpr int EV = 16 / (int)sizeof(S);
   constexpr int64_t TV = (int64_t)kWave * WD * K;
@@ -195,9 +198,9 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   if (vec) {
     scan_device_kernel<F, O, INCL, EV, WD, K><<<grid, block, 0, stream>>>(
-        ia - ph * sizeof(S), oa - ph * sizeof(S), n, ph, ntiles, desc);
+        ia - ph * sizeof(S), oa - ph * sizeof(S), n, n_dev, ph, desc);
   } else {
-    scan_device_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, 0, ntiles,
+    scan_device_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, n_dev, 0,
                                                                         desc);
   }
   return hipGetLastError();
@@ -209,30 +212,31 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
 // microseconds of latency, and registers (not LDS) bound the tile size.
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, bool incl, void* scratch,
-                               hipStream_t stream) {
-  return incl ? launch_dev_cfg<F, O, true, 7, 16>(in, out, n, scratch, stream)
-              : launch_dev_cfg<F, O, false, 7, 16>(in, out, n, scratch, stream);
+                               hipStream_t stream, const int32_t* n_dev) {
+  return incl ? launch_dev_cfg<F, O, true, 7, 16>(in, out, n, scratch, stream, n_dev)
+              : launch_dev_cfg<F, O, false, 7, 16>(in, out, n, scratch, stream, n_dev);
 }
 
 template <class F>
 static hipError_t launch_dev_f(const void* in, void* out, int64_t n, int op, bool incl,
-                               void* scratch, hipStream_t stream) {
+                               void* scratch, hipStream_t stream, const int32_t* n_dev) {
   switch (op) {
-    case 0: return launch_dev_t<F, Op::Add>(in, out, n, incl, scratch, stream);
-    case 1: return launch_dev_t<F, Op::Min>(in, out, n, incl, scratch, stream);
-    default: return launch_dev_t<F, Op::Max>(in, out, n, incl, scratch, stream);
+    case 0: return launch_dev_t<F, Op::Add>(in, out, n, incl, scratch, stream, n_dev);
+    case 1: return launch_dev_t<F, Op::Min>(in, out, n, incl, scratch, stream, n_dev);
+    default: return launch_dev_t<F, Op::Max>(in, out, n, incl, scratch, stream, n_dev);
   }
 }
 
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
-                              bool inclusive, void* scratch, hipStream_t stream) {
+                              bool inclusive, void* scratch, hipStream_t stream,
+                              const int32_t* n_dev) {
   switch (fmt) {
-    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, inclusive, scratch, stream);
-    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, inclusive, scratch, stream);
-    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, inclusive, scratch, stream);
-    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, inclusive, scratch, stream);
-    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, inclusive, scratch, stream);
-    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream);
+    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream, n_dev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -37,9 +37,10 @@ template <> struct Bits<8> { using T = uint64_t; };
 
 template <int EB, int E, bool FVEC, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
-                                                         uintptr_t out_base, int64_t n, int64_t ph,
-                                                         int64_t out_ph, int64_t ntiles,
-                                                         int32_t* num_out, uint64_t* desc) {
+                                                         uintptr_t out_base, int64_t n_cap,
+                                                         const int32_t* n_dev, int64_t ph,
+                                                         int64_t out_ph, int32_t* num_out,
+                                                         uint64_t* desc) {
   using T = typename Bits<EB>::T;
   constexpr int EO = 16 / EB;                     // elements per 16-byte output vector
   constexpr int kThreads = kWave * (WD + 1);
@@ -56,7 +57,13 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
+  const int64_t n = live_count(n_cap, n_dev);
   const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  const int64_t ntiles = n == 0 ? 0 : v_last / kTileVecs + 1;   // tiles holding live elements
+  if (tile >= ntiles) {                              // past the live count: nothing to do
+    if (n == 0 && tile == 0 && threadIdx.x == 0) *num_out = 0;
+    return;
+  }
   if (threadIdx.x == 0) {
     s_posted = 0u;
     s_agg_done = 0u;
@@ -247,7 +254,8 @@ __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
 // lane per tile.
 template <int EB, int WD, int K>
 static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                                 int64_t n, void* scratch, hipStream_t stream) {
+                                 int64_t n, void* scratch, hipStream_t stream,
+                                 const int32_t* n_dev) {
   constexpr int E = 16 / EB;
   constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
@@ -263,10 +271,10 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
   const uintptr_t ibase = ia - (uintptr_t)ph * EB, obase = oa - (uintptr_t)out_ph * EB;
   if (fvec) {
     select_kernel<EB, E, true, WD, K><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
+        ibase, fbase, obase, n, n_dev, ph, out_ph, num_out, desc);
   } else {
     select_kernel<EB, E, false, WD, K><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, ph, out_ph, ntiles, num_out, desc);
+        ibase, fbase, obase, n, n_dev, ph, out_ph, num_out, desc);
   }
   return hipGetLastError();
 }
@@ -278,18 +286,20 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
 // at p = 0.01) but loses at high (620 us at p = 0.99), so stores are staged.
 template <int EB>
 static hipError_t launch_sel_t(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                               int64_t n, void* scratch, hipStream_t stream) {
-  return launch_sel_cfg<EB, 3, 12>(in, flags, out, num_out, n, scratch, stream);
+                               int64_t n, void* scratch, hipStream_t stream,
+                               const int32_t* n_dev) {
+  return launch_sel_cfg<EB, 3, 12>(in, flags, out, num_out, n, scratch, stream, n_dev);
 }
 
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
-                         int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream) {
+                         int64_t n, size_t elem_bytes, void* scratch, hipStream_t stream,
+                         const int32_t* n_dev) {
   if (n == 0) {
     store_count_zero_kernel<<<dim3(1), dim3(1), 0, stream>>>(num_out);
     return hipGetLastError();
   }
-  if (elem_bytes == 4) return launch_sel_t<4>(in, flags, out, num_out, n, scratch, stream);
-  return launch_sel_t<8>(in, flags, out, num_out, n, scratch, stream);
+  if (elem_bytes == 4) return launch_sel_t<4>(in, flags, out, num_out, n, scratch, stream, n_dev);
+  return launch_sel_t<8>(in, flags, out, num_out, n, scratch, stream, n_dev);
 }
 
 }  // namespace sca

@@ -241,3 +241,37 @@ def test_radix_sort_validation():
     assert call(kd=u64, tk=KEY + 8 * n - 8, sb=L.radix_sort_scratch_bytes(n, u64)) == EALIAS
     # 64-bit keys take 8 passes and have their own tile size
     assert L.radix_sort_scratch_bytes(n, u64) > 0
+
+
+def test_devn_validation():
+    L = sc.lib()
+    i32, u32 = D["i32"], D["u32"]
+    cap = 1000
+    need = L.scan_device_scratch_bytes(cap, i32)
+    NL = B + 0x100000                                  # the device count, away from everything
+    assert L.scan_device_devn(A, B, None, cap, i32, OP["add"], S, need, None) == EINVAL
+    assert L.scan_device_devn(A, B, NL + 2, cap, i32, OP["add"], S, need, None) == EINVAL
+    assert L.scan_device_devn(A, B, B + 40, cap, i32, OP["add"], S, need, None) == EALIAS  # in out
+    assert L.scan_device_devn(A, B, S + 64, cap, i32, OP["add"], S, need, None) == EALIAS  # in scratch
+    assert L.scan_device_inclusive_devn(A, B, B + 8, cap, i32, OP["max"], S, need, None) == EALIAS
+    assert L.scan_device_devn(A, B, NL, cap, i32, OP["add"], S, need - 1, None) == ESCRATCH
+    rneed = L.reduce_device_scratch_bytes(cap, i32)
+    assert L.reduce_device_devn(A, B, None, cap, i32, OP["add"], S, rneed, None) == EINVAL
+    assert L.reduce_device_devn(A, B, B, cap, i32, OP["add"], S, rneed, None) == EALIAS   # in out
+    kneed = L.reduce_by_key_scratch_bytes(cap)
+    assert L.reduce_by_key_devn(A, A + 0x10000, B, B + 0x10000, B + 0x20000, None, cap, i32, i32,
+                                S, kneed, None) == EINVAL
+    assert L.reduce_by_key_devn(A, A + 0x10000, B, B + 0x10000, B + 0x20000, B + 0x20000, cap,
+                                i32, i32, S, kneed, None) == EALIAS      # the count is num_runs
+    sneed = L.radix_sort_scratch_bytes(cap, u32)
+    assert L.radix_sort_devn(A, A + 0x100000, None, None, NL, cap, u32, 0, 24, S, sneed,
+                             None) == EINVAL                            # odd pass count
+    assert L.radix_sort_devn(A, A + 0x100000, None, None, None, cap, u32, 0, 32, S, sneed,
+                             None) == EINVAL
+    assert L.radix_sort_devn(A, A + 0x100000, None, None, A + 8, cap, u32, 0, 32, S, sneed,
+                             None) == EALIAS                            # the count is a key
+    cneed = L.select_compact_scratch_bytes(cap)
+    assert L.select_compact_devn(A, S + 0x10000, B, B + 0x10000, None, cap, 4, S, cneed,
+                                 None) == EINVAL
+    assert L.select_compact_devn(A, S + 0x10000, B, B + 0x10000, B + 0x10000, cap, 4, S, cneed,
+                                 None) == EALIAS                        # the count is num_out
