@@ -76,6 +76,8 @@ KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (
     "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, false, 4, 7, 16>(": ("dev_i32_add",
                                                                               "scan_device"),
     "void sca::reduce_partials_kernel<sca::FmtI32, (sca::Op)0, 4>(": ("reduce_i32_add", "reduce"),
+    "void sca::reduce_by_key_kernel<sca::FmtU32, sca::FmtF32, 4, 7, 8>(": ("reduce_by_key",
+                                                                         "reduce_by_key"),
     "void sca::select_kernel<4, 4, true, 3, 12>(": ("select_p0.5", "select"),
     "(anonymous namespace)::copy16_kernel": ("copy16", None),
 }
@@ -437,7 +439,7 @@ def main():
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
     traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
     for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select"),
-                      ("reduce_i32_add", "reduce")):
+                      ("reduce_i32_add", "reduce"), ("reduce_by_key", "reduce_by_key")):
         t = traffic_bytes(key, kind)
         if key in results and t is not None:
             results[key]["traffic_bytes"] = t
