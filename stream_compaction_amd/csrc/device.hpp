@@ -203,6 +203,22 @@ __device__ __forceinline__ W wave_shift_excl(W incl) {
   return dpp<kWaveShr1, 0xf>(incl, identity<O, W>());
 }
 
+// Keeps v in registers as computed here: the compiler may not sink the
+// arithmetic that produced it past this point (used to finish in-place
+// updates before a barrier, so that their inputs die early).
+template <class W>
+__device__ __forceinline__ void materialize(W& v) {
+  if constexpr (sizeof(W) == 8) {
+    uint64_t u = __builtin_bit_cast(uint64_t, v);
+    asm volatile("" : "+v"(u));
+    v = __builtin_bit_cast(W, u);
+  } else {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    asm volatile("" : "+v"(u));
+    v = __builtin_bit_cast(W, u);
+  }
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 // Wave index within the workgroup, as a wave-uniform (scalar) value so that
 // addresses and buffer resources derived from it stay in scalar registers.
@@ -229,6 +245,7 @@ __device__ __forceinline__ int wave_id() {
 // vectors element by element, touching only valid elements.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // A global-memory (address space 1) pointer to T at integer address a.  Going
 // through it, rather than a generic pointer, makes the compiler emit global_*
@@ -249,6 +266,11 @@ struct Buf {
 };
 
 constexpr int kNT = 2;  // nontemporal cache policy for streaming loads
+// Cache policy of full-vector buffer stores.
+#ifndef SCA_STORE_AUX
+#define SCA_STORE_AUX 2
+#endif
+constexpr int kStoreAux = SCA_STORE_AUX;
 
 template <class S, int E>
 struct VecIO {
@@ -319,6 +341,30 @@ struct VecIO {
       d[2] = (uint32_t)b; d[3] = (uint32_t)(b >> 32);
     }
     return uint4{d[0], d[1], d[2], d[3]};
+  }
+
+  // Narrow y and store it as the full vector at byte offset off of buffer b
+  // (one nontemporal buffer store).  The offset always travels in the VGPR
+  // operand with a zero soffset: with an SGPR soffset the compiler assumes
+  // the store-data hazard cannot occur and lets the next instruction
+  // overwrite the data registers at once, and on MI355X such stores were
+  // measured to write some lanes' data from the following instruction.
+  template <class F>
+  static __device__ __forceinline__ void store_full(const Buf& b, uint32_t off,
+                                                    const typename F::W (&y)[E]) {
+    if constexpr (E == 1) {
+      const S s = narrow<F>(y[0]);
+      if constexpr (sizeof(S) == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, s), b.r, off, 0, kStoreAux);
+      } else if constexpr (sizeof(S) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), b.r, off, 0, kStoreAux);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, s), b.r, off, 0, kStoreAux);
+      }
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack<F>(y)), b.r, off, 0,
+                                             kStoreAux);
+    }
   }
 
   // Narrow y and store the elements of vector v that lie in [lo, hi).

@@ -31,8 +31,8 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below (7 data waves x 16
-// loads x 64 lanes); scratch is sized for it.
+// Scratch is sized for tiles of at least this many vectors (7 x 16 x 64; the
+// launch shape below, 11 data waves x 12 loads x 64 lanes, has 8448).
 constexpr int64_t kDevMinTileVecs = 7168;
 
 template <class F, Op O, bool INCL, int E, int WD, int K>
@@ -85,8 +85,10 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
     typename IO::Raw raw[K];
     load(wb, raw);
+    // x[j][k] ends as the combine of this wave's elements before element k of
+    // the lane's vector j (exclusive) or up to it (inclusive), computed in
+    // place so that only the tile's own data stays live across the barrier
     W x[K][E];
-    W pre[K];
     W carry = id;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -94,27 +96,43 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
 #pragma unroll
       for (int k = 1; k < E; ++k) x[j][k] = combine<O>(x[j][k - 1], x[j][k]);
       const W incl = wave_scan_incl<O>(x[j][E - 1]);
-      pre[j] = combine<O>(carry, wave_shift_excl<O>(incl));
+      const W pre = combine<O>(carry, wave_shift_excl<O>(incl));
       carry = combine<O>(carry, readlane(incl, kWave - 1));
+      if constexpr (INCL) {
+#pragma unroll
+        for (int k = 0; k < E; ++k) x[j][k] = combine<O>(pre, x[j][k]);
+      } else {
+#pragma unroll
+        for (int k = E - 1; k > 0; --k) x[j][k] = combine<O>(pre, x[j][k - 1]);
+        x[j][0] = pre;
+      }
+#pragma unroll
+      for (int k = 0; k < E; ++k) materialize(x[j][k]);
     }
     if (lane == 0) post_wave_total<O, W, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done, desc);
     __syncthreads();  // sleeps in hardware until the look-back wave has the prefix
     W wp = s_prefix;
     for (int w = 0; w < wave; ++w) wp = combine<O>(wp, s_wave[w]);
+    if (wb * E >= lo && (wb + kWaveVecs) * E <= hi) {   // wave-uniform: all vectors full
+      // one buffer per 4 KiB of the run, so every store takes the lane's
+      // offset plus an immediate one (a single offset register)
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const W q = combine<O>(wp, pre[j]);
-      W y[E];
-      if constexpr (INCL) {
+      for (int j = 0; j < K; ++j) {
+        const Buf ob(out_base + (wb + (j & ~3) * kWave) * VB, 4 * kWave * VB);
+        W y[E];
 #pragma unroll
-        for (int k = 0; k < E; ++k) y[k] = combine<O>(q, x[j][k]);
-      } else {
-        y[0] = q;
-#pragma unroll
-        for (int k = 1; k < E; ++k) y[k] = combine<O>(q, x[j][k - 1]);
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(wp, x[j][k]);
+        IO::template store_full<F>(ob, (uint32_t)(((j & 3) * kWave + lane) * VB), y);
       }
-      const int64_t v = wb + j * kWave + lane;
-      if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        W y[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(wp, x[j][k]);
+        const int64_t v = wb + j * kWave + lane;
+        if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+      }
     }
   } else {
     // ---- look-back wave ----
@@ -126,17 +144,27 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     };
     W prefix = id;
     if (tile > 0) {
-      // fallback for a late predecessor: reduce its input in element order
+      // fallback for a late predecessor: reduce its input in element order,
+      // a few loads at a time (this rare path must not raise the kernel's
+      // register count, which sets how many workgroups fit on a CU)
       auto reduce_tile = [&](int64_t t) -> W {
+        constexpr int kG = 4;
+        static_assert(kTileVecs % (kG * kWave) == 0, "whole groups of loads");
+        const int64_t first = t * kTileVecs;
+        const int64_t left = v_last + 1 - first;
+        const int64_t nv = left <= 0 ? 0 : (left < kTileVecs ? left : kTileVecs);
+        const Buf buf(in_base + first * VB, nv * VB);
         W acc = id;
-        for (int c = 0; c < WD; ++c) {
-          typename IO::Raw r[K];
-          const int64_t first = t * kTileVecs + c * kWaveVecs;
-          load(first, r);
+#pragma unroll 1
+        for (int g = 0; g < (int)(kTileVecs / (kG * kWave)); ++g) {
+          typename IO::Raw r[kG];
 #pragma unroll
-          for (int j = 0; j < K; ++j) {
+          for (int j = 0; j < kG; ++j)
+            r[j] = IO::load(buf, (uint32_t)(((g * kG + j) * kWave + lane) * VB));
+#pragma unroll
+          for (int j = 0; j < kG; ++j) {
             W y[E];
-            unpack(first + j * kWave, r[j], y);
+            unpack(first + (g * kG + j) * kWave, r[j], y);
 #pragma unroll
             for (int k = 1; k < E; ++k) y[k] = combine<O>(y[k - 1], y[k]);
             acc = combine<O>(acc, readlane(wave_scan_incl<O>(y[E - 1]), kWave - 1));
@@ -206,15 +234,19 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   return hipGetLastError();
 }
 
-// Launch shape measured on MI355X over 2^28 32-bit elements (us per scan):
-// 7 data waves x 16 loads (112 KiB tiles) 411, 3 x 20: 416, 3 x 16: 436,
-// 4 x 16: 525, 3 x 8: 527.  Few, large tiles win: each tile's look-back costs
-// microseconds of latency, and registers (not LDS) bound the tile size.
+// Launch shape measured on MI355X (us per scan; i32 add over 2^28 / i64 min
+// over 2^26): 11 data waves x 12 loads (132 KiB tiles) 365.8 / 208.3,
+// 7 x 16: 374.2 / 215.4 (3 workgroups per CU; 368.2 when capped at 2),
+// 7 x 20: 369.6, 8 x 16: 370.4 / 292.3, 15 x 8: 424.0 / 264.4.  An earlier
+// sweep over 3 and 4 data waves was slower still (3 x 16: 436).  Few, large
+// tiles win, since each look-back costs microseconds of latency; but more
+// resident tiles per CU (a wider address window in flight) lose, so the
+// shape is also chosen for two workgroups per CU.
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, bool incl, void* scratch,
                                hipStream_t stream, const int32_t* n_dev) {
-  return incl ? launch_dev_cfg<F, O, true, 7, 16>(in, out, n, scratch, stream, n_dev)
-              : launch_dev_cfg<F, O, false, 7, 16>(in, out, n, scratch, stream, n_dev);
+  return incl ? launch_dev_cfg<F, O, true, 11, 12>(in, out, n, scratch, stream, n_dev)
+              : launch_dev_cfg<F, O, false, 11, 12>(in, out, n, scratch, stream, n_dev);
 }
 
 template <class F>

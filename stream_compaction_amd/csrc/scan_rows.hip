@@ -93,10 +93,8 @@ __global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, 
     }
 
     // 3. outputs
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
+    auto out_vec = [&](int j, W (&y)[E]) {
       const W q = combine<O>(wp, pre[j]);
-      W y[E];
       if constexpr (EXCL) {
         y[0] = q;
 #pragma unroll
@@ -105,8 +103,24 @@ __global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, 
 #pragma unroll
         for (int k = 0; k < E; ++k) y[k] = combine<O>(q, x[j][k]);
       }
-      const int64_t v = wb + j * kWave + lane;
-      if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+    };
+    if (wb * E >= lo && (wb + kWaveVecs) * E <= hi) {   // wave-uniform: all vectors full
+      // one buffer per 4 KiB of the run (the lane's offset plus an immediate)
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const Buf ob(out_base + (wb + (j & ~3) * kWave) * VB, 4 * kWave * VB);
+        W y[E];
+        out_vec(j, y);
+        IO::template store_full<F>(ob, (uint32_t)(((j & 3) * kWave + lane) * VB), y);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        W y[E];
+        out_vec(j, y);
+        const int64_t v = wb + j * kWave + lane;
+        if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+      }
     }
   }
 }
