@@ -5,21 +5,34 @@
 // The page's own realization is three phases (exclusive scan of the flags
 // into an n-entry index buffer, scatter, one-thread count; section "Under the
 // hood").  Here one kernel does all of it in a single pass, with the scan of
-// the flag counts done by the same DPP wave scan and decoupled look-back as
-// the device-wide scan, and no index buffer.  Workgroup b owns tile b; it has
-// WD data waves and one look-back wave:
-//   1. each data wave loads 16-byte payload vectors (load j of lane l is
-//      vector j*64 + l of its run) and the matching flag bytes, and forms a
-//      bit mask of its selected elements;
-//   2. lane counts are scanned across the wave (DPP) and posted to LDS; the
-//      last data wave to post publishes the tile's count; the look-back wave,
-//      walking back over the predecessors' descriptors from the start, then
-//      publishes the tile's inclusive count and hands over the tile's output
-//      offset G; the tile with the last id writes num_out;
-//   3. selected elements are packed into LDS at their rank, shifted so LDS
-//      vectors line up with 16-byte vectors of `out`, and the workgroup
-//      stores the packed run [G, G + count) with 16-byte stores (element
-//      stores only for the partial vectors at its two ends).
+// the flag counts done by DPP wave scans and the same decoupled look-back as
+// the device-wide scan, and no index buffer.
+//
+// A tile's count depends on its flag bytes alone, so the tile is ordered
+// around them.  Workgroup b owns tile b: WD data waves and one look-back wave.
+// Each data wave owns a run of C chunks; a chunk is J 16-byte payload vectors
+// per lane (load j of lane l is vector j*64 + l of the chunk, so one load
+// instruction covers 1 KiB).
+//   1. A data wave loads the flags of its whole run (E bytes per payload
+//      vector), forms the selection masks, and posts its count; the last data
+//      wave to post publishes the tile's count, one flag round trip after the
+//      tile starts.  It then issues the payload loads of its first chunks.
+//      A lane loads a payload vector only when one of its elements is
+//      selected: the other lanes point the load past the buffer's end, where
+//      it reads zero without touching memory, so at low selectivity most of
+//      the payload is never fetched.
+//   2. The look-back wave walks back over the predecessors' descriptors from
+//      the start, publishes the tile's inclusive count and hands over the
+//      tile's output offset; the tile with the last id writes num_out.
+//   3. Each data wave then streams its chunks, keeping the payload of the next
+//      two chunks in flight: ranks within the chunk come from DPP scans of the
+//      lane counts; the selected elements are packed into the wave's own LDS
+//      staging area at their rank, shifted so LDS vectors line up with 16-byte
+//      vectors of `out`, and the wave stores the chunk's run with 16-byte
+//      stores (element stores only for the partial vectors at its two ends).
+//      Unselected elements are written to a per-lane discard slot, and stores
+//      without data point past the buffer's end, so every chunk issues the
+//      same instructions whatever the flags hold.
 // Elements move as raw bits, so any 4- or 8-byte type (NaN payloads
 // included) is copied exactly.  out past the count is never written.
 #include "device.hpp"
@@ -27,29 +40,41 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below (3 data waves x 12
-// loads x 64 lanes); scratch is sized for it.
-constexpr int64_t kSelMinTileVecs = 2304;
-
 template <int EB> struct Bits;
 template <> struct Bits<4> { using T = uint32_t; };
 template <> struct Bits<8> { using T = uint64_t; };
 
-template <int EB, int E, bool FVEC, int WD, int K>
+constexpr int kSelJ = 4;   // payload vectors per lane per chunk
+
+// Scratch is sized for tiles of at least this many 16-byte payload vectors
+// (the launch shape below: 8 data waves x 8 chunks x 4 loads x 64 lanes).
+constexpr int64_t kSelMinTileVecs = 16384;
+
+// A buffer offset far past any buffer's range: loads there read zero and
+// stores are dropped, without a memory access.  It stays below 2^32 after the
+// compiler adds an immediate offset (at most 4095), so it cannot wrap into
+// the range.
+constexpr uint32_t kOffNone = 0x80000000u;
+
+template <int EB, bool FVEC, int WD, int C>
 __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base, uintptr_t flags_base,
                                                          uintptr_t out_base, int64_t n_cap,
                                                          const int32_t* n_dev, int64_t ph,
                                                          int64_t out_ph, int32_t* num_out,
                                                          uint64_t* desc) {
   using T = typename Bits<EB>::T;
-  constexpr int EO = 16 / EB;                     // elements per 16-byte output vector
-  constexpr int kThreads = kWave * (WD + 1);
-  constexpr int64_t kWaveVecs = (int64_t)kWave * K;
+  constexpr int E = 16 / EB;                      // elements per 16-byte vector
+  constexpr int J = kSelJ;
+  constexpr int64_t kChunkVecs = (int64_t)kWave * J;
+  constexpr int64_t kWaveVecs = kChunkVecs * C;
   constexpr int64_t kTileVecs = kWaveVecs * WD;
   static_assert(kTileVecs >= kSelMinTileVecs, "scratch is sized for the smallest tile");
-  constexpr int kTileElems = (int)kTileVecs * E;
-  constexpr int64_t VB = (int64_t)E * EB;
-  __shared__ __attribute__((aligned(16))) T s_stage[kTileElems + EO];
+  // staging slots per wave: one chunk of elements plus the shift of its start
+  constexpr int kStage = (int)kChunkVecs * E + E;
+  constexpr int kStageVecs = kStage / E;
+  constexpr int kStoreIters = (kStageVecs + kWave - 1) / kWave;
+  __shared__ __attribute__((aligned(16))) T s_stage[WD][kStage];
+  __shared__ T s_discard[WD][kWave];
   __shared__ uint32_t s_wave[WD];
   __shared__ uint32_t s_prefix;
   __shared__ uint32_t s_posted;   // data waves whose counts are in s_wave
@@ -70,116 +95,121 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   }
   __syncthreads();
 
-  // Flag bytes of the run of 64*K vectors starting at `first` (E bytes per
-  // vector, packed low byte first; zero past v_last).
-  auto load_flags = [&](int64_t first, uint32_t (&f)[K]) {
-    const int64_t left = v_last + 1 - first;
-    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
-    const Buf fbuf(flags_base + first * E, nv * E);
+  // Flag bytes of payload vector u of buffer fb, whose first element is
+  // window element e0 (E bytes, low byte first; zero past the buffer's range).
+  // Aligned flags load whole naturally aligned words; otherwise bytes are
+  // loaded one by one, and only those of live elements, so no byte outside
+  // the flags array is read.
+  auto flag_word = [&](const Buf& fb, uint32_t u, int64_t e0) -> uint32_t {
+    if constexpr (FVEC && E == 4) {
+      (void)e0;
+      return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(fb.r, u * 4, 0, kNT);
+    } else if constexpr (FVEC && E == 2) {
+      (void)e0;
+      return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(fb.r, u * 2, 0, kNT);
+    } else {
+      uint32_t f = 0u;
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const uint32_t u = (uint32_t)(j * kWave + lane);
-      if constexpr (FVEC && E == 4) {
-        f[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(fbuf.r, u * 4, 0, kNT);
-      } else if constexpr (FVEC && E == 2) {
-        f[j] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(fbuf.r, u * 2, 0, kNT);
-      } else {
-        f[j] = 0u;
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-          f[j] |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(fbuf.r, u * E + k, 0, kNT)
-                  << (8 * k);
+      for (int k = 0; k < E; ++k) {
+        const bool live = e0 + k >= lo && e0 + k < hi;
+        f |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(
+                 fb.r, live ? u * E + k : kOffNone, 0, kNT)
+             << (8 * k);
       }
+      return f;
     }
   };
-  // Selection mask (bit k = element k) of the lane's vector in load j.
-  auto select_mask = [&](int64_t jv, uint32_t f) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int k = 0; k < E; ++k) m |= (((f >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << k;
-    if (!(jv * E >= lo && (jv + kWave) * E <= hi)) {   // wave-uniform: some vector is partial
+  // Selection bits of one payload vector from its flag word f: bit 8k + 7 is
+  // set when flag byte k is nonzero (per byte, (b & 0x7f) + 0x7f sets bit 7
+  // for any nonzero low bits and never carries into the next byte).  With
+  // jv the first vector of its load (wave-uniform) and `full` telling that
+  // every element of the wave's run is live, elements outside [lo, hi) are
+  // cleared only on the slow path.
+  constexpr uint32_t kTop = E == 4 ? 0x80808080u : 0x8080u;   // bit 7 of each flag byte
+  auto sel_bits = [&](int64_t jv, uint32_t f, bool full) {
+    uint32_t t = (((f & 0x7f7f7f7fu) + 0x7f7f7f7fu) | f) & kTop;
+    if (!full && !(jv * E >= lo && (jv + kWave) * E <= hi)) {   // wave-uniform
       const int64_t e0 = (jv + lane) * E;
-      const int64_t ks = lo - e0, ke = hi - e0;
-      const uint32_t start = ks <= 0 ? 0u : (ks >= E ? (uint32_t)E : (uint32_t)ks);
-      const uint32_t end = ke <= 0 ? 0u : (ke >= E ? (uint32_t)E : (uint32_t)ke);
-      m &= ((1u << end) - 1u) & ~((1u << start) - 1u);
+      uint32_t live = 0u;
+#pragma unroll
+      for (int k = 0; k < E; ++k) live |= (e0 + k >= lo && e0 + k < hi ? 1u : 0u) << (8 * k + 7);
+      t &= live;
     }
-    return m;
+    return t;
+  };
+  // The buffer over `len` vectors of the run starting at vector `first`
+  // (clamped to the live vectors), for an array of `vb`-byte vectors at `base`.
+  auto run_buf = [&](uintptr_t base, int64_t vb, int64_t first, int64_t len) {
+    const int64_t left = v_last + 1 - first;
+    const int64_t nv = left <= 0 ? 0 : (left < len ? left : len);
+    return Buf(base + first * vb, nv * vb);
   };
 
-  // 1. payload and selection masks (data waves): every load is issued
-  //    unconditionally through buffer resources that end at the wave's last
-  //    valid vector (past it: zero bits, i.e. unselected); only the two end
-  //    vectors of the array need masking
-  const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this wave's first vector
-  T x[K][E];
-  uint32_t m[K];
-  uint32_t pre[K];
-  if (wave < WD) {
-    uint32_t f[K];
-    {
-      const int64_t left = v_last + 1 - wb;
-      const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
-      const Buf pbuf(in_base + wb * VB, nv * VB);
+  const int64_t wb = tile * kTileVecs + wave * kWaveVecs;  // this data wave's first vector
+  // sb[c]: selection bits of chunk c; element k of the lane's vector j is
+  // selected when bit 8k + 7 - j is set
+  uint32_t sb[C];
+  u32x4 pay[C][J];         // payload (only the chunks in flight are live)
+  const Buf pbuf = run_buf(in_base, 16, wb, kWaveVecs);
+  auto load_chunk = [&](int c) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const uint32_t u = (uint32_t)(j * kWave + lane);
-        if constexpr (E == 1) {
-          if constexpr (EB == 4) {
-            x[j][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(pbuf.r, u * 4, 0, kNT);
-          } else {
-            x[j][0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(pbuf.r, u * 8, 0, kNT));
-          }
-        } else {
-          const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, u * 16, 0, kNT));
-          if constexpr (EB == 4) {
-            x[j][0] = r.x; x[j][1] = r.y; x[j][2] = r.z; x[j][3] = r.w;
-          } else {
-            x[j][0] = ((uint64_t)r.y << 32) | r.x;
-            x[j][1] = ((uint64_t)r.w << 32) | r.z;
-          }
-        }
-      }
+    for (int j = 0; j < J; ++j) {
+      const uint32_t off = (uint32_t)(((c * J + j) * kWave + lane) * 16);
+      const bool any = (sb[c] & (kTop >> j)) != 0u;
+      pay[c][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, any ? off : kOffNone, 0, kNT));
     }
-    load_flags(wb, f);
-#pragma unroll
-    for (int j = 0; j < K; ++j) m[j] = select_mask(wb + j * kWave, f[j]);
+  };
 
-    // 2. ranks within the wave; the wave's count goes to LDS
-    uint32_t carry = 0u;
+  if (wave < WD) {
+    // 1. flags of the whole run -> selection bits -> the wave's count
+    const Buf fbuf = run_buf(flags_base, E, wb, kWaveVecs);
+    const bool full = wb * E >= lo && (wb + kWaveVecs) * E <= hi;   // every element live
+    uint32_t f[C][J];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const uint32_t incl = wave_scan_incl<Op::Add>((uint32_t)__builtin_popcount(m[j]));
-      pre[j] = carry + wave_shift_excl<Op::Add>(incl);
-      carry += readlane(incl, kWave - 1);
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int u = (c * J + j) * kWave + lane;
+        f[c][j] = flag_word(fbuf, (uint32_t)u, (wb + u) * E);
+      }
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      sb[c] = 0u;
+#pragma unroll
+      for (int j = 0; j < J; ++j) sb[c] |= sel_bits(wb + (c * J + j) * kWave, f[c][j], full) >> j;
+      cnt += (uint32_t)__builtin_popcount(sb[c]);
     }
+    const uint32_t total = readlane(wave_scan_incl<Op::Add>(cnt), kWave - 1);
     if (lane == 0) {
-      post_wave_total<Op::Add, uint32_t, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done,
+      post_wave_total<Op::Add, uint32_t, WD>(total, wave, tile, s_wave, &s_posted, &s_agg_done,
                                              desc);
     }
+    load_chunk(0);
+    if constexpr (C > 1) load_chunk(1);
   } else {
-    // 2'. the look-back wave: walks back from the start and, once the last
-    //     data wave has published the tile's count, publishes the tile's
-    //     inclusive count and hands over the output offset
-    auto tile_count = [&]() {
-      uint32_t a = 0u;
-#pragma unroll
-      for (int w = 0; w < WD; ++w) a += s_wave[w];
-      return a;
-    };
+    // 2. the look-back wave: walks back from the start and, once the last
+    //    data wave has published the tile's count, publishes the tile's
+    //    inclusive count and hands over the output offset
     uint32_t prefix = 0u;
     if (tile > 0) {
-      // fallback for a late predecessor: count its selected flags
+      // fallback for a late predecessor: count its selected flags, one chunk
+      // (J loads) at a time
       auto reduce_tile = [&](int64_t t) -> uint32_t {
         uint32_t acc = 0u;
-        for (int c = 0; c < WD; ++c) {
-          const int64_t first = t * kTileVecs + c * kWaveVecs;
-          uint32_t g[K];
-          load_flags(first, g);
-          uint32_t cnt = 0u;
+#pragma unroll 1
+        for (int g = 0; g < WD * C; ++g) {
+          const int64_t first = t * kTileVecs + (int64_t)g * kChunkVecs;
+          const Buf fb = run_buf(flags_base, E, first, kChunkVecs);
+          uint32_t c = 0u;
 #pragma unroll
-          for (int j = 0; j < K; ++j) cnt += (uint32_t)__builtin_popcount(select_mask(first + j * kWave, g[j]));
-          acc += readlane(wave_scan_incl<Op::Add>(cnt), kWave - 1);
+          for (int j = 0; j < J; ++j)
+            c += (uint32_t)__builtin_popcount(sel_bits(
+                first + j * kWave,
+                flag_word(fb, (uint32_t)(j * kWave + lane), (first + j * kWave + lane) * E),
+                false));
+          acc += readlane(wave_scan_incl<Op::Add>(c), kWave - 1);
         }
         return acc;
       };
@@ -187,50 +217,99 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     }
     while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
     if (lane == 0) {
-      const uint32_t agg = tile_count();
+      uint32_t agg = 0u;
+#pragma unroll
+      for (int w = 0; w < WD; ++w) agg += s_wave[w];
       Desc<uint32_t>::publish(desc, tile, kInc, prefix + agg);
       s_prefix = prefix;
       if (tile == ntiles - 1) *num_out = (int32_t)(prefix + agg);
     }
   }
   __syncthreads();
+  if (wave >= WD) return;
 
-  // 3. pack the selected elements into LDS, then store the run with 16-byte vectors
-  const int64_t g = (int64_t)s_prefix;                 // output offset of this tile
-  uint32_t before = 0u, count = 0u;
+  // 3. stream the chunks: rank, pack into LDS, store the run
+  uint32_t r0 = s_prefix;                    // output index of the chunk's first selected element
+  for (int w = 0; w < wave; ++w) r0 += s_wave[w];
+  r0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);   // wave-uniform: buffer bases use it
+  T* const stage = s_stage[wave];
 #pragma unroll
-  for (int w = 0; w < WD; ++w) {
-    const uint32_t c = s_wave[w];
-    before += (w < wave) ? c : 0u;
-    count += c;
-  }
-  const int s0 = (int)((g + out_ph) % EO);             // slot of the first selected element
-  if (wave < WD) {
+  for (int c = 0; c < C; ++c) {
+    if (c + 2 < C) load_chunk(c + 2);
+    const int s = (int)(((int64_t)r0 + out_ph) % E);   // stage slot of the first element
+    // ranks: the chunk's elements are ordered load by load, then lane by
+    // lane.  The lane's J counts (at most E each) are packed in bytes and
+    // scanned exclusively in one pass: a byte then sums at most 63 lanes'
+    // counts (at most 252), so bytes never carry into each other.
+    uint32_t cpk = 0u;
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      uint32_t r = (uint32_t)s0 + before + pre[j];
+    for (int j = 0; j < J; ++j)
+      cpk |= (uint32_t)__builtin_popcount(sb[c] & (kTop >> j)) << (8 * j);
+    const uint32_t ex = wave_scan_incl<Op::Add>(dpp<kWaveShr1, 0xf>(cpk, 0u));
+    const uint32_t e63 = readlane(ex, kWave - 1), c63 = readlane(cpk, kWave - 1);
+    uint32_t pos[J];
+    uint32_t run = (uint32_t)s;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      pos[j] = run + ((ex >> (8 * j)) & 0xffu);
+      run += ((e63 >> (8 * j)) & 0xffu) + ((c63 >> (8 * j)) & 0xffu);
+    }
+    const int end = (int)run;                 // one past the last staged slot
+    // pack: selected elements to their slots, the others to the discard slot
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const u32x4 r = pay[c][j];
+      T x[E];
+      if constexpr (EB == 4) {
+        x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+      } else {
+        x[0] = ((uint64_t)r.y << 32) | r.x;
+        x[1] = ((uint64_t)r.w << 32) | r.z;
+      }
+      uint32_t p = pos[j];
 #pragma unroll
       for (int k = 0; k < E; ++k) {
-        if ((m[j] >> k) & 1u) s_stage[r++] = x[j][k];
+        const bool sel = (sb[c] >> (8 * k + 7 - j)) & 1u;
+        *(sel ? &stage[p] : &s_discard[wave][lane]) = x[k];
+        p += sel ? 1u : 0u;
       }
     }
-  }
-  __syncthreads();
-  const int64_t gv0 = (g + out_ph) / EO;               // first output vector of the run
-  const int end = s0 + (int)count;
-  const int nvec = (end + EO - 1) / EO;
-  for (int w = (int)threadIdx.x; w < nvec; w += kThreads) {
-    const int slot0 = w * EO;
-    const uintptr_t dst = out_base + (uintptr_t)(gv0 + w) * 16;
-    if (slot0 >= s0 && slot0 + EO <= end) {
-      __builtin_nontemporal_store(*(const u32x4*)&s_stage[slot0], gptr<u32x4>(dst));
-    } else {
+    // a wave's LDS operations complete in order; wait for the writes before
+    // the reads of other lanes' slots
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // store stage vectors [0, nvec) to output vectors g0 + q
+    const int64_t g0 = ((int64_t)r0 + out_ph) / E;
+    const int nvec = (end + E - 1) / E;
+    const Buf ob(out_base + g0 * 16, (int64_t)nvec * 16);
 #pragma unroll
-      for (int k = 0; k < EO; ++k) {
-        const int slot = slot0 + k;
-        if (slot >= s0 && slot < end) *gptr<T>(dst + (uintptr_t)k * EB) = s_stage[slot];
+    for (int i = 0; i < kStoreIters; ++i) {
+      const int q = lane + i * kWave;
+      const bool full = q * E >= s && (q + 1) * E <= end;
+      const int qr = q < kStageVecs ? q : kStageVecs - 1;
+      const u32x4 v = *(const u32x4*)&stage[qr * E];
+      __builtin_amdgcn_raw_buffer_store_b128(v, ob.r, full ? (uint32_t)(q * 16) : kOffNone, 0,
+                                             kStoreAux);
+    }
+    // the partial vectors: the first (lane 0) and the last (lane 1), element by element
+    {
+      const int q = lane == 0 ? 0 : nvec - 1;
+      const bool partial = (lane == 0 || (lane == 1 && nvec > 1)) && nvec > 0 &&
+                           !(q * E >= s && (q + 1) * E <= end);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int slot = q * E + k;
+        const bool ok = partial && slot >= s && slot < end;
+        const T v = stage[ok ? slot : 0];
+        const uint32_t off = ok ? (uint32_t)(slot * EB) : kOffNone;
+        if constexpr (EB == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(v, ob.r, off, 0, kStoreAux);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ob.r, off, 0,
+                                                kStoreAux);
+        }
       }
     }
+    r0 += (uint32_t)(end - s);
   }
 }
 
@@ -250,14 +329,14 @@ size_t select_tiles(int64_t n, size_t elem_bytes) {
 
 __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
 
-// One launch shape: WD data waves (plus the look-back wave), K vectors per
-// lane per tile.
-template <int EB, int WD, int K>
+// One launch shape: WD data waves (plus the look-back wave), C chunks per
+// data wave.
+template <int EB, int WD, int C>
 static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                                  int64_t n, void* scratch, hipStream_t stream,
                                  const int32_t* n_dev) {
   constexpr int E = 16 / EB;
-  constexpr int64_t TV = (int64_t)kWave * WD * K;
+  constexpr int64_t TV = (int64_t)kWave * kSelJ * C * WD;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
   const int64_t ph = (int64_t)((ia % 16) / EB);
   const int64_t out_ph = (int64_t)((oa % 16) / EB);
@@ -270,25 +349,20 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ibase = ia - (uintptr_t)ph * EB, obase = oa - (uintptr_t)out_ph * EB;
   if (fvec) {
-    select_kernel<EB, E, true, WD, K><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, n_dev, ph, out_ph, num_out, desc);
+    select_kernel<EB, true, WD, C><<<grid, block, 0, stream>>>(ibase, fbase, obase, n, n_dev, ph,
+                                                              out_ph, num_out, desc);
   } else {
-    select_kernel<EB, E, false, WD, K><<<grid, block, 0, stream>>>(
-        ibase, fbase, obase, n, n_dev, ph, out_ph, num_out, desc);
+    select_kernel<EB, false, WD, C><<<grid, block, 0, stream>>>(ibase, fbase, obase, n, n_dev, ph,
+                                                               out_ph, num_out, desc);
   }
   return hipGetLastError();
 }
 
-// Launch shape measured on MI355X over 2^28 f32 elements (us at p = 0.01 /
-// 0.5 / 0.99): 3 data waves x 12 loads, staged through 48 KiB of LDS,
-// 402 / 466 / 556; 3 x 16: 426 / 486 / 537; 7 x 8: 468 / 510 / 597.  Storing
-// straight from registers instead of staging wins at low selectivity (328 us
-// at p = 0.01) but loses at high (620 us at p = 0.99), so stores are staged.
 template <int EB>
 static hipError_t launch_sel_t(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                                int64_t n, void* scratch, hipStream_t stream,
                                const int32_t* n_dev) {
-  return launch_sel_cfg<EB, 3, 12>(in, flags, out, num_out, n, scratch, stream, n_dev);
+  return launch_sel_cfg<EB, 8, 8>(in, flags, out, num_out, n, scratch, stream, n_dev);
 }
 
 hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
