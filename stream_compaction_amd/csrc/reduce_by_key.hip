@@ -164,16 +164,38 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     const int64_t wb = tile * kTileVecs + wave * kWaveVecs;
     Raw rk[K], rv[K];
     load(wb, rk, rv);
+    // Wave-uniform: every element of the run is live, and the run holds
+    // neither the array's first element (a run start without a key
+    // comparison) nor its last (which closes the last run).  Such waves, all
+    // but the first and last of the array, skip every per-element index test.
+    const bool full = wb * E > lo && (wb + kWaveVecs) * E < hi;
     uint32_t prev = key_at(k_base, wb * E - 1, lo, hi);
-    uint32_t hb[K];
+    static_assert(K * E <= 32, "head bits of the run fit one word");
+    uint32_t hb = 0u;            // bit j*E + k: element k of the lane's vector in load j starts a run
     W pre[K];
     W carry = id;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int64_t jv = wb + j * kWave;
-      hb[j] = heads(jv, rk[j], prev);
+      uint32_t h;
+      W t = id;
+      if (full) {
+        const uint32_t before = dpp<kWaveShr1, 0xf>(elem<E>(rk[j], E - 1), prev);
+        h = 0u;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const uint32_t p = k == 0 ? before : elem<E>(rk[j], k - 1);
+          const uint32_t b = KeyEq<KF>::eq(elem<E>(rk[j], k), p) ? 0u : 1u;
+          h |= b << k;
+          t = combine<Op::Add>(t, W(b, __builtin_bit_cast(V, elem<E>(rv[j], k))));
+        }
+      } else {
+        h = heads(jv, rk[j], prev);
+        t = lane_total(jv, rv[j], h);
+      }
+      hb |= h << (j * E);
       prev = readlane(elem<E>(rk[j], E - 1), kWave - 1);
-      const W incl = wave_scan_incl<Op::Add>(lane_total(jv, rv[j], hb[j]));
+      const W incl = wave_scan_incl<Op::Add>(t);
       pre[j] = combine<Op::Add>(carry, wave_shift_excl<Op::Add>(incl));
       carry = combine<Op::Add>(carry, readlane(incl, kWave - 1));
     }
@@ -183,25 +205,43 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     __syncthreads();
     W wp = s_prefix;
     for (int w = 0; w < wave; ++w) wp = combine<Op::Add>(wp, s_wave[w]);
+    // With the exclusive state st of a run-starting element: its key opens
+    // run st.c, and run st.c - 1 (if any) closed with sum st.s.  (Run indices
+    // never reach n; the bound only keeps every store inside the caller's
+    // n-element outputs whatever the input.)
+    auto emit = [&](const W& st, uint32_t key) {
+      if (st.c < (uint64_t)n) {
+        *gptr<uint32_t>(keys_out + (uintptr_t)st.c * 4) = key;
+        if (st.c > 0) *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+      }
+    };
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int64_t jv = wb + j * kWave;
-      W st = combine<Op::Add>(wp, pre[j]);
+      for (int j = 0; j < K; ++j) {
+        W st = combine<Op::Add>(wp, pre[j]);
 #pragma unroll
-      for (int k = 0; k < E; ++k) {
-        const int64_t i = (jv + lane) * E + k;
-        const uint32_t h = (hb[j] >> k) & 1u;
-        // (run indices never reach n; the bound only keeps every store
-        // inside the caller's n-element outputs whatever the input)
-        if (h && st.c < (uint64_t)n) {
-          *gptr<uint32_t>(keys_out + (uintptr_t)st.c * 4) = elem<E>(rk[j], k);
-          if (st.c > 0) *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+        for (int k = 0; k < E; ++k) {
+          const uint32_t h = (hb >> (j * E + k)) & 1u;
+          if (h) emit(st, elem<E>(rk[j], k));
+          st = combine<Op::Add>(st, W(h, __builtin_bit_cast(V, elem<E>(rv[j], k))));
         }
-        st = combine<Op::Add>(st, W(h, value(rv[j], k, i)));
-        // the last element closes the last run
-        if (i == hi - 1 && st.c >= 1 && st.c <= (uint64_t)n) {
-          *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
-          *gptr<int32_t>(num_runs) = (int32_t)st.c;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t jv = wb + j * kWave;
+        W st = combine<Op::Add>(wp, pre[j]);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const int64_t i = (jv + lane) * E + k;
+          const uint32_t h = (hb >> (j * E + k)) & 1u;
+          if (h) emit(st, elem<E>(rk[j], k));
+          st = combine<Op::Add>(st, W(h, value(rv[j], k, i)));
+          // the last element closes the last run
+          if (i == hi - 1 && st.c >= 1 && st.c <= (uint64_t)n) {
+            *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+            *gptr<int32_t>(num_runs) = (int32_t)st.c;
+          }
         }
       }
     }
@@ -215,17 +255,30 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     };
     W prefix = id;
     if (tile > 0) {
-      // fallback for a late predecessor: fold its input in element order
+      // fallback for a late predecessor: fold its input in element order, a
+      // few loads at a time (this rare path must not raise the kernel's
+      // register count, which sets how many workgroups fit on a CU)
       auto reduce_tile = [&](int64_t t) -> W {
+        constexpr int kG = 2;
+        static_assert(kTileVecs % (kG * kWave) == 0, "whole groups of loads");
+        const int64_t first = t * kTileVecs;
+        const int64_t left = v_last + 1 - first;
+        const int64_t nv = left <= 0 ? 0 : (left < kTileVecs ? left : kTileVecs);
+        const Buf bk(k_base + first * VB, nv * VB), bv(v_base + first * VB, nv * VB);
         W acc = id;
-        uint32_t prev = key_at(k_base, t * kTileVecs * E - 1, lo, hi);
-        for (int c = 0; c < WD; ++c) {
-          Raw rk[K], rv[K];
-          const int64_t first = t * kTileVecs + c * kWaveVecs;
-          load(first, rk, rv);
+        uint32_t prev = key_at(k_base, first * E - 1, lo, hi);
+#pragma unroll 1
+        for (int g = 0; g < (int)(kTileVecs / (kG * kWave)); ++g) {
+          Raw rk[kG], rv[kG];
 #pragma unroll
-          for (int j = 0; j < K; ++j) {
-            const int64_t jv = first + j * kWave;
+          for (int j = 0; j < kG; ++j) {
+            const uint32_t off = (uint32_t)(((g * kG + j) * kWave + lane) * VB);
+            rk[j] = IO::load(bk, off);
+            rv[j] = IO::load(bv, off);
+          }
+#pragma unroll
+          for (int j = 0; j < kG; ++j) {
+            const int64_t jv = first + (g * kG + j) * kWave;
             const uint32_t h = heads(jv, rk[j], prev);
             prev = readlane(elem<E>(rk[j], E - 1), kWave - 1);
             acc = combine<Op::Add>(
