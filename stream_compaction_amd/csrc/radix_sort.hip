@@ -124,7 +124,8 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   static_assert(kThreads >= kRxBins, "one thread per digit");
   __shared__ uint32_t s_wcnt[WAVES][kRxBins];   // per wave: running count, then exclusive prefix
   __shared__ uint32_t s_start[kRxBins];         // the digit's first slot in the tile
-  __shared__ uint32_t s_g[kRxBins];             // the digit's first output position
+  __shared__ uint32_t s_g[kRxBins];             // the digit's first output position (then
+                                                // that minus its first slot in the tile)
   __shared__ uint32_t s_sum[4];
   __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
   KT* s_keys = (KT*)s_buf;
@@ -160,12 +161,20 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const bool valid = dg[j] < 256u;
-    uint64_t match = __ballot(valid);
+    // lanes whose digit equals this lane's: for each digit bit, keep the
+    // lanes that agree with it, match &= ~(ballot ^ sext(bit)), as one
+    // three-input bit operation per 32-bit half (gfx950 v_bitop3_b32)
+    const uint64_t v = __ballot(valid);
+    uint32_t mlo = (uint32_t)v, mhi = (uint32_t)(v >> 32);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint64_t bb = __ballot((dg[j] >> b) & 1u);
-      match &= ((dg[j] >> b) & 1u) ? bb : ~bb;
+      const uint32_t sx = (uint32_t)__builtin_amdgcn_sbfe((int)dg[j], b, 1);   // 0 or ~0
+      const uint64_t bb = __ballot(sx != 0u);
+      // 0x90 is the truth table of a & ~(b ^ c) over operands (a, b, c)
+      mlo = __builtin_amdgcn_bitop3_b32(mlo, (uint32_t)bb, sx, 0x90);
+      mhi = __builtin_amdgcn_bitop3_b32(mhi, (uint32_t)(bb >> 32), sx, 0x90);
     }
+    const uint64_t match = ((uint64_t)mhi << 32) | mlo;
     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0u));
     const uint32_t same = (uint32_t)__builtin_popcountll(match);
@@ -193,6 +202,8 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
     uint32_t off = 0u;
     for (int w = 0; w < wave; ++w) off += s_sum[w];
     s_start[tid] += off;
+    // the digit's output position minus its first slot in the tile
+    s_g[tid] -= s_start[tid];
   }
   __syncthreads();
 
@@ -217,8 +228,8 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
     if (slot < count) {
       const KT key = s_keys[slot];
       const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
-      const int64_t g = (int64_t)s_g[d] + (slot - (int)s_start[d]);
-      if (g >= 0 && g < n) {
+      const uint32_t g = s_g[d] + (uint32_t)slot;     // modulo 2^32, like the offsets
+      if (g < (uint64_t)n) {
         dst[m] = (int32_t)g;
         *gptr<KT>((uintptr_t)(kout + g)) = key;
       }
