@@ -49,6 +49,9 @@ def parse_args():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="merge into profiles/pmc_traffic.json the counter_collection.csv files "
                          "of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--pmc-select-key", default="select_p0.5",
+                    help="workload the select kernel's counters are filed under in this summary "
+                         "(the profiled command ran only that select workload)")
     ap.add_argument("--pmc-command", default="", help="the profiled command, recorded with --pmc-summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed steps of the headline workload")
@@ -83,7 +86,7 @@ KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (
 }
 
 
-def pmc_summary(fetch_csv, write_csv, command):
+def pmc_summary(fetch_csv, write_csv, command, select_key="select_p0.5"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, merged into
     profiles/pmc_traffic.json (kernels absent from these CSVs keep their entries)."""
     import csv
@@ -97,6 +100,7 @@ def pmc_summary(fetch_csv, write_csv, command):
                 name = row["Kernel_Name"]
                 for prefix, (key, _) in KERNEL_KEYS.items():
                     if name.startswith(prefix):
+                        key = select_key if key == "select_p0.5" else key
                         acc.setdefault(key, []).append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
@@ -109,6 +113,7 @@ def pmc_summary(fetch_csv, write_csv, command):
     out["copy16"] = {"bytes": 268435456, "fetch_kib": fetch["copy16"],
                      "write_kib": write["copy16"], "command": command}
     for prefix, (key, kind) in KERNEL_KEYS.items():
+        key = select_key if key == "select_p0.5" else key
         if kind and key in fetch and key in write:
             out["kernels"][key] = {"fetch_kib": fetch[key], "write_kib": write[key],
                                    "source_sha": sources_sha(kind), "command": command,
@@ -141,7 +146,8 @@ def traffic_bytes(key, kind):
 def main():
     args = parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary[:2], command=args.pmc_command)
+        pmc_summary(*args.pmc_summary[:2], command=args.pmc_command,
+                    select_key=args.pmc_select_key)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the library has no multi-GPU "
@@ -385,9 +391,20 @@ def main():
         wall, per = timed(lambda i: sc.select_compact(xp, xf, yo, num, ss), K, W)
         k = int(num.item())
         r = record(name, nsel, nsel * 5 + 4 * k + 4, wall, per, K,
-                   "algorithmic bytes = 4n payload + n flags read, 4k written, 4 count")
+                   "algorithmic bytes = 4n payload + n flags read, 4k written, 4 count (what a "
+                   "kernel that reads every payload element moves).  The kernel loads a payload "
+                   "vector only if one of its elements is selected, so at low p it moves fewer "
+                   "bytes and this figure can exceed the HBM peak; min_bytes counts the flags, "
+                   "the 128-byte payload lines (the L2 line, the unit HBM reads are counted in) "
+                   "that hold a selected element, and the output")
         r["kept"] = k
         r["read_n_plus_write_n_GBps"] = nsel * 8 / (r["kernel_ms_avg"] * 1e-3) / 1e9
+        lines = int(fl[: nsel // 32 * 32].reshape(-1, 32).any(axis=1).sum())
+        if nsel % 32:
+            lines += int(fl[nsel // 32 * 32:].any())
+        r["min_bytes"] = nsel + 128 * lines + 4 * k + 4
+        r["min_bytes_GBps"] = r["min_bytes"] / (r["kernel_ms_avg"] * 1e-3) / 1e9
+        r["min_bytes_frac_of_peak"] = r["min_bytes_GBps"] / PEAK_GBS
         del xp, xf, yo
 
     # ---------------- copy ceiling over the headline's bytes ----------------
@@ -439,6 +456,7 @@ def main():
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
     traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
     for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select"),
+                      ("select_p0.01", "select"),
                       ("reduce_i32_add", "reduce"), ("reduce_by_key", "reduce_by_key")):
         t = traffic_bytes(key, kind)
         if key in results and t is not None:
