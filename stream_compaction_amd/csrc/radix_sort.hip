@@ -290,23 +290,34 @@ static hipError_t rx_copy(const void* src, void* dst, size_t bytes, hipStream_t 
   return hipGetLastError();
 }
 
-// Tile shape per key width: 8 waves; 16 keys per thread for 32-bit keys, 8 for
-// 64-bit keys (the LDS reorder buffer holds one tile of the wider of key and
+// Tile shape per key and value width.  32-bit keys alone: 8 waves x 16 keys
+// per thread (8192 keys).  32-bit keys with 4-byte values: 16 waves x 16
+// (16384 keys, one workgroup per CU by LDS): the longer digit runs halve the
+// write streams per key, which measured 7.40 ms against 8.79 ms for 2^28
+// key-value pairs, while costing the keys-only sort (5.31 ms against 4.19)
+// its occupancy.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys: 8
+// waves x 8 (the LDS reorder buffer holds one tile of the wider of key and
 // value).
-template <class KT> struct RxShape;
-template <> struct RxShape<uint32_t> { static constexpr int kWaves = 8, kKpt = 16; };
-template <> struct RxShape<uint64_t> { static constexpr int kWaves = 8, kKpt = 8; };
+template <class KT, int VB> struct RxShape { static constexpr int kWaves = 8, kKpt = 8; };
+template <> struct RxShape<uint32_t, 0> { static constexpr int kWaves = 8, kKpt = 16; };
+template <> struct RxShape<uint32_t, 4> { static constexpr int kWaves = 16, kKpt = 16; };
+template <> struct RxShape<uint32_t, 8> { static constexpr int kWaves = 8, kKpt = 16; };
 
-template <class KT>
+template <class KT, int VB>
 constexpr int64_t rx_tile() {
-  return (int64_t)64 * RxShape<KT>::kWaves * RxShape<KT>::kKpt;
+  return (int64_t)64 * RxShape<KT, VB>::kWaves * RxShape<KT, VB>::kKpt;
 }
 
 // Scratch layout: the digit-major tile histograms (ntiles * 256 u32), their
 // exclusive scan (the same size), then the device-wide scan's own scratch.
-static int64_t rx_ntiles(int64_t n, size_t key_bytes) {
-  const int64_t tile = key_bytes == 8 ? rx_tile<uint64_t>() : rx_tile<uint32_t>();
-  return (n + tile - 1) / tile;
+// Sized for the smallest tile of the key width, so one size serves every
+// value width.
+static int64_t rx_ntiles(int64_t n, int64_t tile) { return (n + tile - 1) / tile; }
+static int64_t rx_min_tile(size_t key_bytes) {
+  if (key_bytes == 8) return rx_tile<uint64_t, 0>();
+  const int64_t a = rx_tile<uint32_t, 0>(), b = rx_tile<uint32_t, 4>(), c = rx_tile<uint32_t, 8>();
+  const int64_t m = a < b ? a : b;
+  return m < c ? m : c;
 }
 
 static size_t rx_hist_bytes(int64_t ntiles) {
@@ -315,7 +326,7 @@ static size_t rx_hist_bytes(int64_t ntiles) {
 
 size_t radix_sort_scratch(int64_t n, size_t key_bytes) {
   if (n <= 1) return 0;
-  const int64_t nt = rx_ntiles(n, key_bytes);
+  const int64_t nt = rx_ntiles(n, rx_min_tile(key_bytes));
   return 2 * rx_hist_bytes(nt) + desc_scratch_bytes(scan_device_tiles(nt * kRxBins, Fmt::U32));
 }
 
@@ -323,12 +334,12 @@ template <class KT, KeyKind KK, int VB>
 static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
                               int end_bit, void* scratch, hipStream_t stream,
                               const int32_t* n_dev) {
-  constexpr int W = RxShape<KT>::kWaves, KPT = RxShape<KT>::kKpt;
+  constexpr int W = RxShape<KT, VB>::kWaves, KPT = RxShape<KT, VB>::kKpt;
   const int npass = end_bit / 8;
   // with a device count the result must land in `keys` by itself (an even
   // number of passes): a copy back would need the count on the host
   if (n_dev != nullptr && npass % 2 == 1) return hipErrorInvalidValue;
-  const int64_t ntiles = rx_ntiles(n, sizeof(KT));
+  const int64_t ntiles = rx_ntiles(n, rx_tile<KT, VB>());
   uint32_t* hist = (uint32_t*)scratch;
   uint32_t* offs = (uint32_t*)((char*)scratch + rx_hist_bytes(ntiles));
   void* scan_scratch = (char*)scratch + 2 * rx_hist_bytes(ntiles);
