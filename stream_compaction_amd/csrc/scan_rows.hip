@@ -132,10 +132,12 @@ static void launch_rows_cfg(uintptr_t in_base, uintptr_t out_base, int64_t rows,
       in_base, out_base, rows, n, ph);
 }
 
-// Launch shape by the number of 16-byte vectors a row touches (measured on
-// MI355X for bf16 rows of 8192 / 8191 elements: four waves of four loads, or
-// five for a ragged row that straddles one more vector, beat both one long
-// wave per row and wide 16-wave groups).
+// Launch shape by the number of 16-byte vectors a row touches, measured on
+// MI355X for bf16 rows of 8192 elements (1024 vectors) and 8191 (1025 when
+// the row straddles one more vector): four waves of four loads for 1024
+// (42.4 us; one or two waves with several chunks per row 46-48 us), six
+// waves of three for up to 1152 (44.9 us, against 48.1 for four waves of
+// five, 46.2 for five of four and 55-56 for nine or ten waves of two).
 template <class F, Op O, bool EXCL, int E>
 static hipError_t launch_rows_e(uintptr_t in_base, uintptr_t out_base, int64_t rows, int64_t n,
                                 int64_t ph, hipStream_t stream) {
@@ -148,6 +150,8 @@ static hipError_t launch_rows_e(uintptr_t in_base, uintptr_t out_base, int64_t r
     launch_rows_cfg<F, O, EXCL, E, 2, 2>(in_base, out_base, rows, n, ph, stream);
   } else if (vmax <= 16 * kWave) {
     launch_rows_cfg<F, O, EXCL, E, 4, 4>(in_base, out_base, rows, n, ph, stream);
+  } else if (vmax <= 18 * kWave) {
+    launch_rows_cfg<F, O, EXCL, E, 6, 3>(in_base, out_base, rows, n, ph, stream);
   } else if (vmax <= 20 * kWave) {
     launch_rows_cfg<F, O, EXCL, E, 4, 5>(in_base, out_base, rows, n, ph, stream);
   } else {
