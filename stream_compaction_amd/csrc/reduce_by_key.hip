@@ -31,9 +31,9 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below (7 data waves x 8
+// Smallest tile (in vectors) of any launch shape below (15 data waves x 8
 // loads x 64 lanes); scratch is sized for it.
-constexpr int64_t kRbkMinTileVecs = 3584;
+constexpr int64_t kRbkMinTileVecs = 7680;
 
 // The scan state of a span: run starts in it and the sum after the last one.
 // V is float for f32 values and uint32_t for i32/u32 values (wrapping).
@@ -161,50 +161,88 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
 
   if (wave < WD) {
     // ---- data wave ----
+    // The keys of the wave's run stay in registers; the values stream in
+    // after the tile's prefix is known.  A span's aggregate (c, s) needs only
+    // its run starts and the values after the last of them, which almost
+    // always lie in the last load: that load's values are fetched with the
+    // keys.
     const int64_t wb = tile * kTileVecs + wave * kWaveVecs;
-    Raw rk[K], rv[K];
-    load(wb, rk, rv);
+    const int64_t left = v_last + 1 - wb;
+    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
+    const Buf bk(k_base + wb * VB, nv * VB), bv(v_base + wb * VB, nv * VB);
+    auto vload = [&](int j) { return IO::load(bv, (uint32_t)((j * kWave + lane) * VB)); };
+    Raw rk[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) rk[j] = IO::load(bk, (uint32_t)((j * kWave + lane) * VB));
+    const Raw rv_last = vload(K - 1);
     // Wave-uniform: every element of the run is live, and the run holds
     // neither the array's first element (a run start without a key
     // comparison) nor its last (which closes the last run).  Such waves, all
     // but the first and last of the array, skip every per-element index test.
     const bool full = wb * E > lo && (wb + kWaveVecs) * E < hi;
     uint32_t prev = key_at(k_base, wb * E - 1, lo, hi);
-    static_assert(K * E <= 32, "head bits of the run fit one word");
-    uint32_t hb = 0u;            // bit j*E + k: element k of the lane's vector in load j starts a run
-    W pre[K];
-    W carry = id;
+    static_assert(K * E <= 64, "head bits of the run fit two words");
+    uint64_t hb = 0u;            // bit j*E + k: element k of the lane's vector in load j starts a run
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int64_t jv = wb + j * kWave;
       uint32_t h;
-      W t = id;
       if (full) {
         const uint32_t before = dpp<kWaveShr1, 0xf>(elem<E>(rk[j], E - 1), prev);
         h = 0u;
 #pragma unroll
         for (int k = 0; k < E; ++k) {
           const uint32_t p = k == 0 ? before : elem<E>(rk[j], k - 1);
-          const uint32_t b = KeyEq<KF>::eq(elem<E>(rk[j], k), p) ? 0u : 1u;
-          h |= b << k;
-          t = combine<Op::Add>(t, W(b, __builtin_bit_cast(V, elem<E>(rv[j], k))));
+          h |= (KeyEq<KF>::eq(elem<E>(rk[j], k), p) ? 0u : 1u) << k;
         }
       } else {
-        h = heads(jv, rk[j], prev);
-        t = lane_total(jv, rv[j], h);
+        h = heads(wb + j * kWave, rk[j], prev);
       }
-      hb |= h << (j * E);
+      hb |= (uint64_t)h << (j * E);
       prev = readlane(elem<E>(rk[j], E - 1), kWave - 1);
-      const W incl = wave_scan_incl<Op::Add>(t);
-      pre[j] = combine<Op::Add>(carry, wave_shift_excl<Op::Add>(incl));
-      carry = combine<Op::Add>(carry, readlane(incl, kWave - 1));
     }
+    // the wave's aggregate: its run starts, and the sum from the last one on
+    // (position (j*64 + lane)*E + k orders the wave's elements)
+    const uint32_t c_w =
+        readlane(wave_scan_incl<Op::Add>((uint32_t)__builtin_popcountll(hb)), kWave - 1);
+    int lastpos = -1;
+    if (hb != 0u) {
+      const int b = 63 - __builtin_clzll(hb);
+      lastpos = ((b / E) * kWave + lane) * E + b % E;
+    }
+    const int p_last = readlane(wave_scan_incl<Op::Max>(lastpos), kWave - 1);
+    // sum of the values of load j from position p_last on (a run start's own
+    // value belongs to its run; with no run start, p_last = -1 takes them all)
+    auto tail_sum = [&](int j, const Raw& rv) -> V {
+      V t = V(0);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int pos = (j * kWave + lane) * E + k;
+        const V v = full ? __builtin_bit_cast(V, elem<E>(rv, k))
+                         : value(rv, k, (wb + j * kWave + lane) * E + k);
+        t = (V)(t + (pos >= p_last ? v : V(0)));
+      }
+      return readlane(wave_scan_incl<Op::Add>(t), kWave - 1);
+    };
+    V s_w = V(0);
+    constexpr int kLastStart = (K - 1) * kWave * E;
+    if (p_last < kLastStart) {                 // rare: the last run started before the last load
+#pragma unroll 1
+      for (int j = (p_last < 0 ? 0 : p_last / (kWave * E)); j < K - 1; ++j)
+        s_w = (V)(s_w + tail_sum(j, vload(j)));
+    }
+    s_w = (V)(s_w + tail_sum(K - 1, rv_last));
     if (lane == 0) {
-      post_wave_total<Op::Add, W, WD>(carry, wave, tile, s_wave, &s_posted, &s_agg_done, desc);
+      post_wave_total<Op::Add, W, WD>(W(c_w, s_w), wave, tile, s_wave, &s_posted, &s_agg_done,
+                                      desc);
     }
+    // the first values stream in while the look-back runs
+    static_assert(K >= 3, "a ring of two values loads ahead");
+    Raw ring[2];
+    ring[0] = vload(0);
+    ring[1] = vload(1);
     __syncthreads();
-    W wp = s_prefix;
-    for (int w = 0; w < wave; ++w) wp = combine<Op::Add>(wp, s_wave[w]);
+    W carry = s_prefix;
+    for (int w = 0; w < wave; ++w) carry = combine<Op::Add>(carry, s_wave[w]);
     // With the exclusive state st of a run-starting element: its key opens
     // run st.c, and run st.c - 1 (if any) closed with sum st.s.  (Run indices
     // never reach n; the bound only keeps every store inside the caller's
@@ -215,28 +253,35 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
         if (st.c > 0) *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
       }
     };
-    if (full) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        W st = combine<Op::Add>(wp, pre[j]);
+    for (int j = 0; j < K; ++j) {
+      const Raw rv = j == K - 1 ? rv_last : ring[j % 2];
+      if (j + 2 < K - 1) ring[j % 2] = vload(j + 2);
+      const int64_t jv = wb + j * kWave;
+      const uint32_t h4 = (uint32_t)(hb >> (j * E)) & ((1u << E) - 1u);
+      W t = id;
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const V v = full ? __builtin_bit_cast(V, elem<E>(rv, k)) : value(rv, k, (jv + lane) * E + k);
+        t = combine<Op::Add>(t, W((h4 >> k) & 1u, v));
+      }
+      const W incl = wave_scan_incl<Op::Add>(t);
+      W st = combine<Op::Add>(carry, wave_shift_excl<Op::Add>(incl));
+      carry = combine<Op::Add>(carry, readlane(incl, kWave - 1));
+      if (full) {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-          const uint32_t h = (hb >> (j * E + k)) & 1u;
+          const uint32_t h = (h4 >> k) & 1u;
           if (h) emit(st, elem<E>(rk[j], k));
-          st = combine<Op::Add>(st, W(h, __builtin_bit_cast(V, elem<E>(rv[j], k))));
+          st = combine<Op::Add>(st, W(h, __builtin_bit_cast(V, elem<E>(rv, k))));
         }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int64_t jv = wb + j * kWave;
-        W st = combine<Op::Add>(wp, pre[j]);
+      } else {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
           const int64_t i = (jv + lane) * E + k;
-          const uint32_t h = (hb >> (j * E + k)) & 1u;
+          const uint32_t h = (h4 >> k) & 1u;
           if (h) emit(st, elem<E>(rk[j], k));
-          st = combine<Op::Add>(st, W(h, value(rv[j], k, i)));
+          st = combine<Op::Add>(st, W(h, value(rv, k, i)));
           // the last element closes the last run
           if (i == hi - 1 && st.c >= 1 && st.c <= (uint64_t)n) {
             *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
@@ -338,8 +383,12 @@ template <class KF, class VF>
 static hipError_t launch_rbk_t(const void* keys, const void* values, void* keys_out,
                                void* values_out, int32_t* num_runs, int64_t n, void* scratch,
                                hipStream_t stream, const int32_t* n_dev) {
-  return launch_rbk_cfg<KF, VF, 7, 8>(keys, values, keys_out, values_out, num_runs, n, scratch,
-                                      stream, n_dev);
+  // Launch shape measured on MI355X over 2^27 pairs in runs of mean length 8
+  // (us): 15 data waves x 8 loads 303.4, 7 x 16 314.4, 15 x 6 314.4,
+  // 7 x 8 332.8, 9 x 12 350.7.  With the keys held and the values streamed,
+  // larger tiles (fewer links in the look-back chain) win.
+  return launch_rbk_cfg<KF, VF, 15, 8>(keys, values, keys_out, values_out, num_runs, n, scratch,
+                                       stream, n_dev);
 }
 
 template <class KF>
