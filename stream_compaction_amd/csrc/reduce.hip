@@ -6,8 +6,8 @@
 //
 // Two launches on the caller's stream, with no atomics, flags or look-back:
 //  1. reduce_partials_kernel: G workgroups of four waves.  The 16-byte
-//     vectors of the aligned window are cut into runs of 64*K vectors (one
-//     run = K loads per lane, each load instruction covering 1 KiB), and the
+//     vectors of the aligned window are cut into runs of 64*L vectors (one
+//     run = L loads per lane, each load instruction covering 1 KiB), and the
 //     runs into 4*G contiguous ranges, one per wave, in wave order.  Each wave
 //     reduces its range; the workgroup combines its four wave totals in wave
 //     order and writes one partial to scratch[b].
@@ -29,13 +29,23 @@
 namespace sca {
 
 constexpr int kRedWaves = 4;          // waves per workgroup of the first launch
-constexpr int kRedLoads = 8;          // 16-byte loads per lane per run
-constexpr int64_t kRedRunVecs = (int64_t)kWave * kRedLoads;
+// 16-byte loads per lane per run, measured on MI355X (us for i32 add 2^28 /
+// f32 add 2^27 / i64 max 2^26 / f32 min 2^27): 16 loads 159 / 85 / 85 / 94,
+// 8 loads 174 / 88 / 88 / 92, 4 loads 174 / 91 / 93 / 96, 24 loads 165 / 85 /
+// 90 / 92, 32 loads 162 / 85 / 84 / 92.  The ordered floating min/max, which
+// scan every load across the wave, keep 8.
+constexpr int kRedLoadsMin = 8;       // the smaller run: the most workgroups, for scratch sizing
+template <class W, Op O>
+constexpr bool red_ordered() {
+  return (O == Op::Min || O == Op::Max) && (std::is_same_v<W, float> || std::is_same_v<W, double>);
+}
+template <class W, Op O>
+constexpr int red_loads() { return red_ordered<W, O>() ? 8 : 16; }
 // Workgroups of the first launch at most (eight per compute unit of MI355X);
 // the final wave then combines at most this many partials.
 constexpr int64_t kRedMaxBlocks = 2048;
 
-template <class F, Op O, int E>
+template <class F, Op O, int E, int L>
 __global__ __launch_bounds__(64 * kRedWaves) void reduce_partials_kernel(
     uintptr_t in_base, int64_t n_cap, const int32_t* n_dev, int64_t ph, int64_t runs_per_wave,
     uintptr_t partials) {
@@ -43,8 +53,8 @@ __global__ __launch_bounds__(64 * kRedWaves) void reduce_partials_kernel(
   using W = typename F::W;
   using IO = VecIO<S, E>;
   constexpr int64_t VB = (int64_t)E * sizeof(S);
-  constexpr bool kOrdered =
-      (O == Op::Min || O == Op::Max) && (std::is_same_v<W, float> || std::is_same_v<W, double>);
+  constexpr bool kOrdered = red_ordered<W, O>();
+  constexpr int64_t kRedRunVecs = (int64_t)kWave * L;
   __shared__ W s_wave[kRedWaves];
 
   const int lane = lane_id(), wave = wave_id();
@@ -62,11 +72,11 @@ __global__ __launch_bounds__(64 * kRedWaves) void reduce_partials_kernel(
     const int64_t left = v_last + 1 - first;
     const int64_t nv = left < kRedRunVecs ? left : kRedRunVecs;
     const Buf buf(in_base + first * VB, nv * VB);
-    typename IO::Raw raw[kRedLoads];
+    typename IO::Raw raw[L];
 #pragma unroll
-    for (int j = 0; j < kRedLoads; ++j) raw[j] = IO::load(buf, (uint32_t)((j * kWave + lane) * VB));
+    for (int j = 0; j < L; ++j) raw[j] = IO::load(buf, (uint32_t)((j * kWave + lane) * VB));
 #pragma unroll
-    for (int j = 0; j < kRedLoads; ++j) {
+    for (int j = 0; j < L; ++j) {
       const int64_t jv = first + j * kWave;
       W x[E];
       if (jv * E >= lo && (jv + kWave) * E <= hi) {    // wave-uniform: all vectors full
@@ -118,11 +128,11 @@ struct RedGeom {
   int64_t runs = 0, runs_per_wave = 0, blocks = 0;
 };
 
-static RedGeom red_geom(int64_t n, int e, int64_t ph) {
+static RedGeom red_geom(int64_t n, int e, int64_t ph, int64_t run_vecs) {
   RedGeom g;
   if (n <= 0) return g;
   const int64_t v_last = (n + ph - 1) / e;
-  g.runs = v_last / kRedRunVecs + 1;
+  g.runs = v_last / run_vecs + 1;
   const int64_t waves_wanted = g.runs;              // at least one run per wave
   int64_t blocks = (waves_wanted + kRedWaves - 1) / kRedWaves;
   if (blocks > kRedMaxBlocks) blocks = kRedMaxBlocks;
@@ -144,7 +154,7 @@ static int fmt_size(Fmt f) {
 
 size_t reduce_partials(int64_t n, Fmt fmt) {
   const int e = 16 / fmt_size(fmt);
-  const int64_t runs = red_geom(n, e, e - 1).runs;
+  const int64_t runs = red_geom(n, e, e - 1, (int64_t)kWave * kRedLoadsMin).runs;
   const int64_t bound = (runs + kRedWaves - 1) / kRedWaves;
   return (size_t)(bound < kRedMaxBlocks ? bound : kRedMaxBlocks);
 }
@@ -156,9 +166,11 @@ static hipError_t launch_red_t(const void* in, void* out, int64_t n, void* scrat
   constexpr int EV = 16 / (int)sizeof(S);
   const uintptr_t ia = (uintptr_t)in;
   const int64_t ph = (int64_t)((ia % 16) / sizeof(S));
-  const RedGeom g = red_geom(n, EV, ph);
+  constexpr int L = red_loads<typename F::W, O>();
+  static_assert(L >= kRedLoadsMin, "scratch is sized for the smallest run");
+  const RedGeom g = red_geom(n, EV, ph, (int64_t)kWave * L);
   if (g.blocks > 0) {
-    reduce_partials_kernel<F, O, EV><<<dim3((unsigned)g.blocks), dim3(64 * kRedWaves), 0, stream>>>(
+    reduce_partials_kernel<F, O, EV, L><<<dim3((unsigned)g.blocks), dim3(64 * kRedWaves), 0, stream>>>(
         ia - (uintptr_t)ph * sizeof(S), n, n_dev, ph, g.runs_per_wave, (uintptr_t)scratch);
   }
   reduce_final_kernel<F, O><<<dim3(1), dim3(64), 0, stream>>>((uintptr_t)scratch, g.blocks,
