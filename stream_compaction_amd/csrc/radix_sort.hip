@@ -112,79 +112,93 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
 template <int VB> struct ValBits { using T = uint32_t; };
 template <> struct ValBits<8> { using T = uint64_t; };
 
-template <class KT, KeyKind KK, int VB, int WAVES, int KPT>
-__global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
+// A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
+// 32-bit, and accesses past the range read zero or are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rx_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(uint32_t)bytes, 0x00020000);
+}
+template <class T>
+__device__ __forceinline__ T rx_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 4) {
+    return (T)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT));
+  }
+}
+template <class T>
+__device__ __forceinline__ void rx_store(__amdgpu_buffer_rsrc_t r, uint32_t off, T x) {
+  if constexpr (sizeof(T) == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)x, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
+  }
+}
+
+// Ranking.  For each load, the lanes holding the same digit are found through
+// a per-wave LDS table of 64-bit lane masks, one entry per digit (and one for
+// "no key"): every lane ORs its lane bit into its digit's entry, reads the
+// entry back and clears it.  LDS work from one wave is carried out in issue
+// order, so the read sees the OR of every lane and the next load's ORs come
+// after the clear.  A lane's rank is the count of such lanes below it plus the
+// wave's running count of the digit, so ranks follow input order.
+//
+// Stores: with B32 the outputs are written through buffer resources with
+// 32-bit byte offsets (every array below 4 GiB); else through 64-bit
+// addresses.  FULL tiles skip every per-key range test.
+template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL>
+__device__ __forceinline__ void rx_scatter_tile(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
-    void* __restrict__ vout_, int64_t n_cap, const int32_t* n_dev, int shift, int64_t ntiles,
-    const uint32_t* __restrict__ offsets) {
+    void* __restrict__ vout_, int64_t n, int shift, int64_t t0, int count,
+    uint32_t (*s_wcnt)[kRxBins + 1], uint32_t* s_start, uint32_t* s_g, uint32_t* s_sum,
+    unsigned char* s_buf) {
   using VT = typename ValBits<VB>::T;
   constexpr int kThreads = 64 * WAVES;
-  constexpr int kTile = kThreads * KPT;
-  constexpr int kBufBytes = kTile * (int)(sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB);
-  static_assert(kThreads >= kRxBins, "one thread per digit");
-  __shared__ uint32_t s_wcnt[WAVES][kRxBins];   // per wave: running count, then exclusive prefix
-  __shared__ uint32_t s_start[kRxBins];         // the digit's first slot in the tile
-  __shared__ uint32_t s_g[kRxBins];             // the digit's first output position (then
-                                                // that minus its first slot in the tile)
-  __shared__ uint32_t s_sum[4];
-  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
+  constexpr int kBins1 = kRxBins + 1;                // digit 256: no key
   KT* s_keys = (KT*)s_buf;
   VT* s_vals = (VT*)s_buf;
-  const VT* vin = (const VT*)vin_;
-  VT* vout = (VT*)vout_;
-
+  uint64_t* s_tab = (uint64_t*)s_buf + wave_id() * kBins1;   // this wave's lane-mask table
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int64_t tile = blockIdx.x;
-  const int64_t t0 = tile * kTile;
-  const int64_t n = live_count(n_cap, n_dev);
-  const int count =                                  // keys in this tile
-      (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
-  for (int i = tid; i < WAVES * kRxBins; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
-  if (tid < kRxBins) s_g[tid] = offsets[(int64_t)tid * ntiles + tile];
-  __syncthreads();
 
-  // ---- load, and rank within the wave (stable: ranks follow input order) ----
+  // ---- load (buffer resources bounded at the tile's keys) ----
   const int wbase = wave * 64 * KPT;                 // the wave's first slot in the tile
+  const auto kr = rx_rsrc(kin + t0, (uint64_t)count * sizeof(KT));
   KT k[KPT];
   VT v[VB != 0 ? KPT : 1];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) k[j] = rx_load<KT>(kr, (uint32_t)((wbase + j * 64 + lane) * sizeof(KT)));
+  if constexpr (VB != 0) {
+    const auto vr = rx_rsrc((const VT*)vin_ + t0, (uint64_t)count * VB);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) v[j] = rx_load<VT>(vr, (uint32_t)((wbase + j * 64 + lane) * VB));
+  }
   uint32_t dg[KPT], rank[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int s = wbase + j * 64 + lane;
-    k[j] = s < count ? *gptr<const KT>((uintptr_t)(kin + t0 + s)) : KT(0);
-    if constexpr (VB != 0) v[j] = s < count ? *gptr<const VT>((uintptr_t)(vin + t0 + s)) : VT(0);
+    dg[j] = (uint32_t)((sort_image<KT, KK>(k[j]) >> shift) & 255u);
+    if constexpr (!FULL) dg[j] = wbase + j * 64 + lane < count ? dg[j] : (uint32_t)kRxBins;
   }
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    dg[j] = wbase + j * 64 + lane < count
-                ? (uint32_t)((sort_image<KT, KK>(k[j]) >> shift) & 255u) : 256u;
+
+  // ---- rank within the wave ----
+  uint32_t* cnt = s_wcnt[wave];
+  const uint64_t lbit = 1ull << lane;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool valid = dg[j] < 256u;
-    // lanes whose digit equals this lane's: for each digit bit, keep the
-    // lanes that agree with it, match &= ~(ballot ^ sext(bit)), as one
-    // three-input bit operation per 32-bit half (gfx950 v_bitop3_b32)
-    const uint64_t v = __ballot(valid);
-    uint32_t mlo = (uint32_t)v, mhi = (uint32_t)(v >> 32);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint32_t sx = (uint32_t)__builtin_amdgcn_sbfe((int)dg[j], b, 1);   // 0 or ~0
-      const uint64_t bb = __ballot(sx != 0u);
-      // 0x90 is the truth table of a & ~(b ^ c) over operands (a, b, c)
-      mlo = __builtin_amdgcn_bitop3_b32(mlo, (uint32_t)bb, sx, 0x90);
-      mhi = __builtin_amdgcn_bitop3_b32(mhi, (uint32_t)(bb >> 32), sx, 0x90);
-    }
-    const uint64_t match = ((uint64_t)mhi << 32) | mlo;
+    uint64_t* e = s_tab + dg[j];
+    __hip_atomic_fetch_or(e, lbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t match = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t old = __hip_atomic_load(cnt + dg[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0u));
     const uint32_t same = (uint32_t)__builtin_popcountll(match);
-    const uint32_t old = valid ? s_wcnt[wave][dg[j]] : 0u;
-    if (valid && below == 0u) s_wcnt[wave][dg[j]] = old + same;
+    // every lane of the digit writes the same new count
+    __hip_atomic_store(cnt + dg[j], old + same, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     rank[j] = old + below;
   }
   __syncthreads();
 
-  // ---- per digit: prefix over waves, and the digit's first slot in the tile ----
+  // ---- per digit: each wave's first slot in the tile ----
   if (tid < kRxBins) {
     uint32_t h = 0u;
 #pragma unroll
@@ -201,37 +215,40 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   if (tid < kRxBins) {
     uint32_t off = 0u;
     for (int w = 0; w < wave; ++w) off += s_sum[w];
-    s_start[tid] += off;
-    // the digit's output position minus its first slot in the tile
-    s_g[tid] -= s_start[tid];
+    const uint32_t st = s_start[tid] + off;           // the digit's first slot in the tile
+    s_g[tid] -= st;                                   // its output position minus that slot
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s_wcnt[w][tid] += st;
   }
   __syncthreads();
 
-  // ---- reorder by digit in LDS, then write every digit's run in place ----
+  // ---- reorder by digit in LDS (the tables are no longer needed) ----
   int lpos[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    lpos[j] = -1;
-    if (dg[j] < 256u) {
-      lpos[j] = (int)(s_start[dg[j]] + s_wcnt[wave][dg[j]] + rank[j]);
-      s_keys[lpos[j]] = k[j];
-    }
+    lpos[j] = (int)(cnt[dg[j]] + rank[j]);
+    if (FULL || dg[j] < (uint32_t)kRxBins) s_keys[lpos[j]] = k[j];
   }
   __syncthreads();
-  // (positions are below n by construction; the bound only keeps every store
-  // inside the output whatever the input)
-  int32_t dst[KPT];
+
+  // ---- write every digit's run in place ----
+  // (positions are below n by construction; the range checks only keep every
+  // store inside the output whatever the input)
+  const auto okr = rx_rsrc(kout, B32 ? (uint64_t)n * sizeof(KT) : 0);
+  uint32_t dst[KPT];
 #pragma unroll
   for (int m = 0; m < KPT; ++m) {
     const int slot = tid + m * kThreads;
-    dst[m] = -1;
-    if (slot < count) {
+    dst[m] = 0xffffffffu;
+    if (FULL || slot < count) {
       const KT key = s_keys[slot];
       const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
       const uint32_t g = s_g[d] + (uint32_t)slot;     // modulo 2^32, like the offsets
-      if (g < (uint64_t)n) {
-        dst[m] = (int32_t)g;
-        *gptr<KT>((uintptr_t)(kout + g)) = key;
+      dst[m] = g;
+      if constexpr (B32) {
+        rx_store<KT>(okr, g * (uint32_t)sizeof(KT), key);
+      } else {
+        if (g < (uint64_t)n) *gptr<KT>((uintptr_t)(kout + g)) = key;
       }
     }
   }
@@ -239,11 +256,71 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
     __syncthreads();                                   // every key is out of the buffer
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (lpos[j] >= 0) s_vals[lpos[j]] = v[j];
+      if (FULL || dg[j] < (uint32_t)kRxBins) s_vals[lpos[j]] = v[j];
     __syncthreads();
+    VT* vout = (VT*)vout_;
+    const auto ovr = rx_rsrc(vout, B32 ? (uint64_t)n * VB : 0);
 #pragma unroll
-    for (int m = 0; m < KPT; ++m)
-      if (dst[m] >= 0) *gptr<VT>((uintptr_t)(vout + dst[m])) = s_vals[tid + m * kThreads];
+    for (int m = 0; m < KPT; ++m) {
+      const int slot = tid + m * kThreads;
+      if (FULL || slot < count) {
+        const VT x = s_vals[slot];
+        if constexpr (B32) {
+          rx_store<VT>(ovr, dst[m] * (uint32_t)VB, x);
+        } else {
+          if (dst[m] < (uint64_t)n) *gptr<VT>((uintptr_t)(vout + dst[m])) = x;
+        }
+      }
+    }
+  }
+}
+
+// Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8).
+// This mapping gives each XCD a contiguous range of tiles, taken in order, so
+// the pieces of a digit's output run that neighbouring tiles write side by
+// side meet in one L2 and leave it as whole lines.
+__device__ __forceinline__ int64_t rx_xcd_tile(int64_t b, int64_t ntiles) {
+  const int64_t q = ntiles / 8, r = ntiles % 8, x = b % 8, i = b / 8;
+  return x * q + (x < r ? x : r) + i;
+}
+
+template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32>
+__global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
+    const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin,
+    void* __restrict__ vout, int64_t n_cap, const int32_t* n_dev, int shift, int64_t ntiles,
+    const uint32_t* __restrict__ offsets) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kTile = kThreads * KPT;
+  constexpr int kBins1 = kRxBins + 1;
+  constexpr int kSortBytes = kTile * (int)(sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB);
+  constexpr int kTabBytes = WAVES * kBins1 * 8;
+  constexpr int kBufBytes = kSortBytes > kTabBytes ? kSortBytes : kTabBytes;
+  static_assert(kThreads >= kRxBins, "one thread per digit");
+  __shared__ uint32_t s_wcnt[WAVES][kBins1];    // per wave: running count, then first slot
+  __shared__ uint32_t s_start[kRxBins];         // the digit's first slot in the tile
+  __shared__ uint32_t s_g[kRxBins];             // the digit's first output position (then
+                                                // that minus its first slot in the tile)
+  __shared__ uint32_t s_sum[kRxBins / 64];
+  // lane-mask tables while ranking, then the tile reordered by digit
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int64_t tile = rx_xcd_tile(blockIdx.x, ntiles);
+  const int64_t t0 = tile * kTile;
+  const int64_t n = live_count(n_cap, n_dev);
+  const int count =                                  // keys in this tile
+      (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
+  for (int i = tid; i < WAVES * kBins1; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
+  uint64_t* tab = (uint64_t*)s_buf + wave * kBins1;
+  for (int i = lane; i < kBins1; i += kWave) tab[i] = 0ull;
+  if (tid < kRxBins) s_g[tid] = offsets[(int64_t)tid * ntiles + tile];
+  __syncthreads();
+  if (count == kTile) {
+    rx_scatter_tile<KT, KK, VB, WAVES, KPT, B32, true>(kin, kout, vin, vout, n, shift, t0, count,
+                                                       s_wcnt, s_start, s_g, s_sum, s_buf);
+  } else {
+    rx_scatter_tile<KT, KK, VB, WAVES, KPT, B32, false>(kin, kout, vin, vout, n, shift, t0, count,
+                                                        s_wcnt, s_start, s_g, s_sum, s_buf);
   }
 }
 
@@ -347,6 +424,8 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
   KT* dst = (KT*)tmp_keys;
   void* vsrc = values;
   void* vdst = tmp_values;
+  // every key and value array below 4 GiB: 32-bit buffer offsets for the scatter
+  const bool b32 = (uint64_t)n * (sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB) < (1ull << 32);
   hipError_t err = hipSuccess;
   for (int p = 0; p < npass; ++p) {
     radix_tile_hist_kernel<KT, KK, W, KPT><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
@@ -356,8 +435,13 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
       err = launch_scan_device(hist, offs, ntiles * kRxBins, Fmt::U32, 0, false, scan_scratch,
                                stream);
     if (err != hipSuccess) return err;
-    radix_scatter_kernel<KT, KK, VB, W, KPT><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
-        src, dst, vsrc, vdst, n, n_dev, 8 * p, ntiles, offs);
+    if (b32) {
+      radix_scatter_kernel<KT, KK, VB, W, KPT, true><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
+          src, dst, vsrc, vdst, n, n_dev, 8 * p, ntiles, offs);
+    } else {
+      radix_scatter_kernel<KT, KK, VB, W, KPT, false><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
+          src, dst, vsrc, vdst, n, n_dev, 8 * p, ntiles, offs);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     KT* ts = src; src = dst; dst = ts;
