@@ -48,6 +48,16 @@ __device__ __forceinline__ KT sort_image(KT k) {
 }
 
 constexpr int kRxBins = 256;
+
+// Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8).
+// This mapping gives each XCD a contiguous range of tiles, taken in order, so
+// what neighbouring tiles write side by side (their histogram counts, the
+// pieces of a digit's output run) meets in one L2 and leaves it as whole
+// lines.
+__device__ __forceinline__ int64_t rx_xcd_tile(int64_t b, int64_t ntiles) {
+  const int64_t q = ntiles / 8, r = ntiles % 8, x = b % 8, i = b / 8;
+  return x * q + (x < r ? x : r) + i;
+}
 // ---------------------------------------------------------------------------
 // 2. one digit pass
 // ---------------------------------------------------------------------------
@@ -64,7 +74,7 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
   static_assert(kThreads >= kRxBins, "one thread per digit");
   __shared__ uint32_t s_h[WAVES][kRxBins];
   const int tid = threadIdx.x, wave = wave_id();
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = rx_xcd_tile(blockIdx.x, ntiles);
   const int64_t t0 = tile * kTile;
   const int64_t n = live_count(n_cap, n_dev);
   const int count = (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
@@ -80,22 +90,29 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
   for (int j = 0; j < kLoads; ++j)
     r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
         buf.r, (uint32_t)(((j * kThreads + tid) * kE) * (int)sizeof(KT)), 0, kNT));
+  auto count_keys = [&](auto full) {
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kLoads; ++j) {
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const int s = (j * kThreads + tid) * kE + e;
-      KT key;
-      if constexpr (sizeof(KT) == 4) {
-        key = r[j][e];
-      } else {
-        key = ((KT)r[j][2 * e + 1] << 32) | r[j][2 * e];
-      }
-      if (s < count) {
-        const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
-        __hip_atomic_fetch_add(&s_h[wave][d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int e = 0; e < kE; ++e) {
+        const int s = (j * kThreads + tid) * kE + e;
+        KT key;
+        if constexpr (sizeof(KT) == 4) {
+          key = r[j][e];
+        } else {
+          key = ((KT)r[j][2 * e + 1] << 32) | r[j][2 * e];
+        }
+        if (decltype(full)::value || s < count) {
+          const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
+          __hip_atomic_fetch_add(&s_h[wave][d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     }
+  };
+  if (count == kTile) {
+    count_keys(std::true_type{});
+  } else {
+    count_keys(std::false_type{});
   }
   __syncthreads();
   if (tid < kRxBins) {
@@ -273,15 +290,6 @@ __device__ __forceinline__ void rx_scatter_tile(
       }
     }
   }
-}
-
-// Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8).
-// This mapping gives each XCD a contiguous range of tiles, taken in order, so
-// the pieces of a digit's output run that neighbouring tiles write side by
-// side meet in one L2 and leave it as whole lines.
-__device__ __forceinline__ int64_t rx_xcd_tile(int64_t b, int64_t ntiles) {
-  const int64_t q = ntiles / 8, r = ntiles % 8, x = b % 8, i = b / 8;
-  return x * q + (x < r ? x : r) + i;
 }
 
 template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32>
