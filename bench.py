@@ -82,6 +82,8 @@ KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (
     "void sca::reduce_by_key_kernel<sca::FmtU32, sca::FmtF32, 4, 15, 8>(": ("reduce_by_key",
                                                                          "reduce_by_key"),
     "void sca::select_kernel<4, true, 8, 8>(": ("select_p0.5", "select"),
+    "void sca::radix_scatter_kernel<unsigned int, (sca::KeyKind)0, 0, 8, 16, true>(": ("sort_u32",
+                                                                                     "radix_sort"),
     "(anonymous namespace)::copy16_kernel": ("copy16", None),
 }
 
@@ -462,6 +464,12 @@ def main():
         if key in results and t is not None:
             results[key]["traffic_bytes"] = t
             results[key]["traffic_over_algorithmic"] = t / results[key]["algorithmic_bytes"]
+    t = traffic_bytes("sort_u32", "radix_sort")
+    if "sort_u32" in results and t is not None:
+        # one digit pass's scatter kernel, against its read + write of the keys
+        per_pass = 8 * results["sort_u32"]["elements"]
+        results["sort_u32"]["scatter_traffic_bytes"] = t
+        results["sort_u32"]["scatter_traffic_over_8n"] = t / per_pass
 
     props = torch.cuda.get_device_properties(dev)
     line = {
