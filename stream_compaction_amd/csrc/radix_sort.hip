@@ -11,12 +11,13 @@
 //      each (digit, tile)'s first output position: all keys with a smaller
 //      digit, plus the keys with this digit in earlier tiles;
 //   3. radix_scatter_kernel: every tile ranks its keys stably within the
-//      tile - for each load, the lanes holding the same digit are found with
-//      eight ballots (one per digit bit), and a lane's rank is the count of
-//      such lanes below it plus the wave's running count of that digit (kept
-//      in LDS), so ranks follow input order - reorders them by digit in LDS,
+//      tile - for each load, the lanes holding the same digit are found
+//      through a per-wave LDS table of lane masks, and a lane's rank is the
+//      count of such lanes below it plus the wave's running count of that
+//      digit, so ranks follow input order - reorders them by digit in LDS,
 //      and writes every digit's run contiguously at its output position;
 //      values follow the same permutation.
+// Both per-tile kernels hand each XCD a contiguous range of tiles.
 // A single-pass variant with a per-digit decoupled look-back (one read of the
 // keys per pass instead of two) was measured slower on MI355X: with ~500
 // tiles resident, each digit's walk waited on predecessors that were still
@@ -71,7 +72,6 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
     uint32_t* hist) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
-  static_assert(kThreads >= kRxBins, "one thread per digit");
   __shared__ uint32_t s_h[WAVES][kRxBins];
   const int tid = threadIdx.x, wave = wave_id();
   const int64_t tile = rx_xcd_tile(blockIdx.x, ntiles);
@@ -115,11 +115,11 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
     count_keys(std::false_type{});
   }
   __syncthreads();
-  if (tid < kRxBins) {
+  for (int d = tid; d < kRxBins; d += kThreads) {
     uint32_t h = 0u;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) h += s_h[w][tid];
-    hist[(int64_t)tid * ntiles + tile] = h;
+    for (int w = 0; w < WAVES; ++w) h += s_h[w][d];
+    hist[(int64_t)d * ntiles + tile] = h;
   }
 }
 
@@ -393,6 +393,19 @@ constexpr int64_t rx_tile() {
   return (int64_t)64 * RxShape<KT, VB>::kWaves * RxShape<KT, VB>::kKpt;
 }
 
+// The histogram kernel's shape: 16-byte loads per lane over the scatter's
+// tile.  Measured per pass over 2^28 u32 keys (tiles of 8,192 / 16,384):
+// 4 loads 180 / 174 us, 8 loads 186 / 179, 16 loads 197 / 186.
+#ifndef SCA_RX_HIST_LOADS
+#define SCA_RX_HIST_LOADS 4
+#endif
+template <class KT, int VB> struct RxHistShape {
+  static constexpr int kKpt = SCA_RX_HIST_LOADS * (16 / (int)sizeof(KT));
+  static constexpr int kWaves = (int)(rx_tile<KT, VB>() / (64 * kKpt));
+  static_assert(kWaves >= 1 && (int64_t)kWaves * 64 * kKpt == rx_tile<KT, VB>(),
+                "the histogram covers the scatter's tile");
+};
+
 // Scratch layout: the digit-major tile histograms (ntiles * 256 u32), their
 // exclusive scan (the same size), then the device-wide scan's own scratch.
 // Sized for the smallest tile of the key width, so one size serves every
@@ -436,7 +449,8 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
   const bool b32 = (uint64_t)n * (sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB) < (1ull << 32);
   hipError_t err = hipSuccess;
   for (int p = 0; p < npass; ++p) {
-    radix_tile_hist_kernel<KT, KK, W, KPT><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(
+    constexpr int HW = RxHistShape<KT, VB>::kWaves, HKPT = RxHistShape<KT, VB>::kKpt;
+    radix_tile_hist_kernel<KT, KK, HW, HKPT><<<dim3((unsigned)ntiles), dim3(64 * HW), 0, stream>>>(
         src, n, n_dev, 8 * p, ntiles, hist);
     err = hipGetLastError();
     if (err == hipSuccess)
