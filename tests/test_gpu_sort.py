@@ -131,3 +131,35 @@ def test_lookback_recovery_build_sort():
     ok, ov = oracle.sort(keys, "u32", np.arange(n, dtype=np.int32))
     check_exact(from_dev(kd, "u32"), ok, "fallback build keys")
     check_exact(vd.cpu().numpy(), ov, "fallback build values")
+
+
+def test_sort_arrays_past_4gib():
+    """Arrays of 4 GiB and more take the scatter's 64-bit-address stores (below
+    that, 32-bit buffer offsets).  At these sizes the check is against the
+    library sort torch ships (stable, in unsigned key order): keys, and the
+    original index carried as an 8-byte value, must match it exactly."""
+    g = torch.Generator(device="cuda").manual_seed(20_000)
+    top = torch.tensor(-(1 << 63), dtype=torch.int64, device="cuda")
+    # u64 keys only, from 997 distinct bit patterns
+    n = (1 << 29) + 7
+    note(f"sort u64 keys only n={n}")
+    alphabet = torch.randint(-(1 << 63), (1 << 63) - 1, (997,), generator=g, device="cuda",
+                             dtype=torch.int64)
+    keys = alphabet[torch.randint(0, 997, (n,), generator=g, device="cuda")]
+    ref = torch.sort(keys ^ top, stable=True).values ^ top
+    sc.radix_sort(keys, key_dtype="u64")
+    torch.cuda.synchronize()
+    assert torch.equal(keys, ref), "u64 keys past 4 GiB"
+    del keys, ref
+    # u32 keys with i64 values (each key's index), from 1,009 distinct keys
+    n = (1 << 29) + 3
+    note(f"sort u32 keys + i64 values n={n}")
+    alpha32 = torch.randint(-(1 << 31), (1 << 31) - 1, (1009,), generator=g, device="cuda",
+                            dtype=torch.int32)
+    keys = alpha32[torch.randint(0, 1009, (n,), generator=g, device="cuda")]
+    vals = torch.arange(n, dtype=torch.int64, device="cuda")
+    ref = torch.sort(keys.to(torch.int64) & 0xFFFFFFFF, stable=True)
+    sc.radix_sort(keys, vals, key_dtype="u32", value_dtype="i64")
+    torch.cuda.synchronize()
+    assert torch.equal(keys.to(torch.int64) & 0xFFFFFFFF, ref.values), "u32 keys past 4 GiB"
+    assert torch.equal(vals, ref.indices), "i64 values past 4 GiB (stability)"
