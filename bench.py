@@ -126,6 +126,56 @@ def pmc_summary(fetch_csv, write_csv, command, select_key="select_p0.5"):
     print(json.dumps(out))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def gpu_facts():
+    """Engine clock, GFX target and cache sizes of the first GPU node in the KFD
+    topology (sysfs), and the ROCm version; each field is None where unreadable."""
+    out = {"max_engine_clock_MHz": None, "gfx_target_version": None, "caches_KiB": None,
+           "rocm": None}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            out["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    base = "/sys/class/kfd/kfd/topology/nodes"
+    try:
+        for node in sorted(os.listdir(base), key=lambda x: int(x) if x.isdigit() else 1 << 30):
+            props = {}
+            with open(os.path.join(base, node, "properties")) as fh:
+                for ln in fh:
+                    k, _, v = ln.partition(" ")
+                    props[k] = v.strip()
+            if int(props.get("gfx_target_version", "0") or 0) == 0:
+                continue                                  # a CPU node
+            out["max_engine_clock_MHz"] = int(props.get("max_engine_clk_fcompute", 0)) or None
+            out["gfx_target_version"] = int(props["gfx_target_version"])
+            levels = {}
+            cdir = os.path.join(base, node, "caches")
+            for c in os.listdir(cdir):
+                cp = {}
+                with open(os.path.join(cdir, c, "properties")) as fh:
+                    for ln in fh:
+                        k, _, v = ln.partition(" ")
+                        cp[k] = v.strip()
+                lvl = f"L{cp.get('level', '?')}"
+                levels[lvl] = max(levels.get(lvl, 0), int(cp.get("size", 0)))
+            out["caches_KiB"] = dict(sorted(levels.items())) or None
+            break
+    except (OSError, ValueError, KeyError):
+        pass
+    return out
+
+
 def traffic_bytes(key, kind):
     """HBM bytes per launch from the stored counter readings, scaled by what the
     same counters read for copy16; None if absent or the kernel changed since."""
@@ -453,7 +503,7 @@ def main():
         cpu = {"value": rows * n / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
                "sample": f"the full workload, bf16 [{rows}, {n}] exclusive add, rows split "
                          f"over {threads} threads, median of 3 runs ({t:.3f} s each)",
-               "cpu": platform.processor() or platform.machine()}
+               "cpu": cpu_model()}
 
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
     traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
@@ -507,7 +557,8 @@ def main():
     line["device"] = {"name": props.name, "cus": props.multi_processor_count,
                       "hbm_GiB": round(props.total_memory / 2**30, 1),
                       "l2_bytes": getattr(props, "L2_cache_size", None),
-                      "torch": torch.__version__, "hip": torch.version.hip}
+                      "arch": getattr(props, "gcnArchName", None),
+                      "torch": torch.__version__, "hip": torch.version.hip, **gpu_facts()}
     print(json.dumps(line), flush=True)
 
 
