@@ -19,7 +19,7 @@
  *    arguments must not overlap (SCAN_EALIAS); this refines the rule that an
  *    exclusive scan's output must be a distinct buffer from its input
  *    ("Algorithms" page, section qd.algorithms.exclusive_scan_{add,min,max},
- *    "No in-place scan").
+ *    its list of constraints).
  *  - Sizes: 0 <= n <= INT32_MAX (the pages index and count with 32-bit
  *    integers: "Algorithms" page, section "Capacity (log256_max_n)", and the
  *    i32 count of select).  n == 0 (or rows == 0) is a valid no-op ("Tile

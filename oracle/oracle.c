@@ -11,7 +11,7 @@
  *
  *  - The left-prefix recurrence of "Tile operations and reductions"
  *    (LuisaCompute), section "Why not just infer it from reduce?":
- *    for an ordered fiber x[0..n) with seed z and combine op,
+ *    the running states of a sequence x[0..n) folded from seed z with op,
  *        p[0] = z,  p[i+1] = op(p[i], x[i]),
  *        inclusive[i] = p[i+1],  exclusive[i] = p[i].
  *    The seed is the identity of (op, dtype) from the "Algorithms" page
