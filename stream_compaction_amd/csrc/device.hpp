@@ -434,25 +434,44 @@ template <class W> struct Desc<W, 4> {
   }
 };
 
+// 64-bit values: words 0-1 hold the aggregate, words 2-3 the inclusive
+// prefix, each word (1 << 32) | half.  A pair is written with one 16-byte
+// store and read with one 16-byte load, with the cache policy of the relaxed
+// agent-scope atomics above (sc1), so both halves normally become visible
+// together: written as two 8-byte stores, a poll that fell between them saw
+// "not ready" and slept a whole pause, which cost 64-bit scans about 15 us
+// of look-back at 2^26 elements.  Each 8-byte half is still single-copy
+// atomic and carries its own flag, so a torn read is simply not ready.
 template <class W> struct Desc<W, 8> {
   static constexpr int kWords = 4;
   static __device__ __forceinline__ void publish(uint64_t* d, int64_t tile, uint32_t status, W v) {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
     uint64_t* slot = d + tile * kDescLineWords + (status == kInc ? 2 : 0);
-    st_relaxed(slot, (1ull << 32) | (uint32_t)u);
-    st_relaxed(slot + 1, (1ull << 32) | (uint32_t)(u >> 32));
+    const u32x4 w = {(uint32_t)u, 1u, (uint32_t)(u >> 32), 1u};
+    // The compiler's hazard checks do not see into asm: the wait states a
+    // store of more than 8 bytes needs before its data registers may be
+    // written again are part of the statement.
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 4" : : "v"(slot), "v"(w)
+                 : "memory");
   }
-  // All four words are loaded together (one round trip, not two).
+  // Both pairs are loaded together (one round trip); the wait is part of the
+  // load, so the poll is issued afresh every time.
   static __device__ __forceinline__ uint32_t read(const uint64_t* d, int64_t tile, W& v) {
     const uint64_t* s = d + tile * kDescLineWords;
-    const uint64_t alo = ld_relaxed(s), ahi = ld_relaxed(s + 1);
-    const uint64_t ilo = ld_relaxed(s + 2), ihi = ld_relaxed(s + 3);
-    if ((ilo >> 32) && (ihi >> 32)) {
-      v = __builtin_bit_cast(W, (ihi << 32) | (uint32_t)ilo);
+    u32x4 a, i;
+    asm volatile(
+        "global_load_dwordx4 %0, %2, off sc1\n\t"
+        "global_load_dwordx4 %1, %2, off offset:16 sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(a), "=&v"(i)
+        : "v"(s)
+        : "memory");
+    if (i.y && i.w) {
+      v = __builtin_bit_cast(W, ((uint64_t)i.z << 32) | i.x);
       return kInc;
     }
-    if ((alo >> 32) && (ahi >> 32)) {
-      v = __builtin_bit_cast(W, (ahi << 32) | (uint32_t)alo);
+    if (a.y && a.w) {
+      v = __builtin_bit_cast(W, ((uint64_t)a.z << 32) | a.x);
       return kAgg;
     }
     return kNone;
