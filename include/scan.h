@@ -214,14 +214,16 @@ scan_status radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_value
  * prefix out[0..k), and k is written to num_out[0] on the device.  The page
  * requires flags to be exactly 0/1; here any nonzero byte selects.  out must
  * hold n elements; out[k..n) is left untouched.  Elements are copied as raw
- * bytes, so any 4- or 8-byte element type works (NaN payloads survive).
+ * bytes, so any element type of 1, 2, 4, 8 or 16 bytes works (NaN payloads
+ * survive; the page allows any scalar or struct element type).
  *
- *   in         device pointer, n elements of elem_bytes bytes.
+ *   in         device pointer, n elements of elem_bytes bytes, aligned to
+ *              elem_bytes (as is out).
  *   flags      device pointer, n bytes (uint8).
  *   out        device pointer, capacity n elements; must not overlap in,
  *              flags, num_out or scratch.
  *   num_out    device pointer to one int32.
- *   elem_bytes 4 or 8 (else SCAN_ENOTSUP).
+ *   elem_bytes 1, 2, 4, 8 or 16 (else SCAN_ENOTSUP).
  *   scratch    >= select_compact_scratch_bytes(n) bytes, 16-byte aligned.
  */
 size_t select_compact_scratch_bytes(int64_t n);

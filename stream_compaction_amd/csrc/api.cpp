@@ -337,13 +337,15 @@ scan_status radix_sort_devn(void* keys, void* tmp_keys, void* values, void* tmp_
 
 size_t select_compact_scratch_bytes(int64_t n) {
   if (n < 0) return 0;
-  return sca::desc_scratch_bytes(sca::select_tiles(n, 8));
+  return sca::desc_scratch_bytes(sca::select_tiles(n, 16));
 }
 
 static scan_status select_any(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                               int64_t n, size_t elem_bytes, void* scratch, size_t scratch_bytes,
                               void* stream, bool devn, const int32_t* n_dev) {
-  if (elem_bytes != 4 && elem_bytes != 8) return SCAN_ENOTSUP;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8 &&
+      elem_bytes != 16)
+    return SCAN_ENOTSUP;
   if (n < 0 || n > kMaxN) return SCAN_EINVAL;
   if (num_out == nullptr || !aligned(num_out, 4)) return SCAN_EINVAL;
   if (n > 0) {

@@ -10,9 +10,10 @@
 //
 // A tile's count depends on its flag bytes alone, so the tile is ordered
 // around them.  Workgroup b owns tile b: WD data waves and one look-back wave.
-// Each data wave owns a run of C chunks; a chunk is J 16-byte payload vectors
-// per lane (load j of lane l is vector j*64 + l of the chunk, so one load
-// instruction covers 1 KiB).
+// Each data wave owns a run of C chunks; a chunk is J payload vectors per lane
+// (load j of lane l is vector j*64 + l of the chunk, so one load instruction
+// covers 64 consecutive vectors).  A vector is 16 bytes for elements of 4, 8
+// and 16 bytes, and four elements (4 or 8 bytes) for elements of 1 and 2.
 //   1. A data wave loads the flags of its whole run (E bytes per payload
 //      vector), forms the selection masks, and posts its count; the last data
 //      wave to post publishes the tile's count, one flag round trip after the
@@ -27,22 +28,65 @@
 //   3. Each data wave then streams its chunks, keeping the payload of the next
 //      two chunks in flight: ranks within the chunk come from DPP scans of the
 //      lane counts; the selected elements are packed into the wave's own LDS
-//      staging area at their rank, shifted so LDS vectors line up with 16-byte
-//      vectors of `out`, and the wave stores the chunk's run with 16-byte
+//      staging area at their rank, shifted so LDS vectors line up with the
+//      vectors of `out`, and the wave stores the chunk's run with whole-vector
 //      stores (element stores only for the partial vectors at its two ends).
 //      Unselected elements are written to a per-lane discard slot, and stores
 //      without data point past the buffer's end, so every chunk issues the
 //      same instructions whatever the flags hold.
-// Elements move as raw bits, so any 4- or 8-byte type (NaN payloads
-// included) is copied exactly.  out past the count is never written.
+// Elements move as raw bits, so any type of 1, 2, 4, 8 or 16 bytes (NaN
+// payloads and structs included) is copied exactly.  out past the count is
+// never written.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace sca {
 
 template <int EB> struct Bits;
+template <> struct Bits<1> { using T = uint8_t; };
+template <> struct Bits<2> { using T = uint16_t; };
 template <> struct Bits<4> { using T = uint32_t; };
 template <> struct Bits<8> { using T = uint64_t; };
+template <> struct Bits<16> { using T = u32x4; };
+
+// Elements per payload vector: four for elements of 1, 2 and 4 bytes (vectors
+// of 4, 8 and 16 bytes), two for 8-byte and one for 16-byte elements.  A
+// vector's flags are then at most 4 bytes, and a lane's count per load at
+// most 4, which the byte-packed rank scan below relies on.
+template <int EB> constexpr int sel_e() { return EB <= 4 ? 4 : 16 / EB; }
+
+// A payload vector of VB bytes as loaded and stored (4, 8 or 16 bytes).
+template <int VB> struct SelVec;
+template <> struct SelVec<4> { using T = uint32_t; };
+template <> struct SelVec<8> { using T = u32x2; };
+template <> struct SelVec<16> { using T = u32x4; };
+
+template <int VB>
+__device__ __forceinline__ typename SelVec<VB>::T sel_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (VB == 4) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT);
+  } else if constexpr (VB == 8) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT));
+  } else {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+  }
+}
+
+// One element (B bytes) or one vector stored at byte offset off.
+template <int B, class V>
+__device__ __forceinline__ void sel_store(V v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (B == 1) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, off, 0, kStoreAux);
+  } else if constexpr (B == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, off, 0, kStoreAux);
+  } else if constexpr (B == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, off, 0, kStoreAux);
+  } else if constexpr (B == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kStoreAux);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kStoreAux);
+  }
+}
 
 constexpr int kSelJ = 4;   // payload vectors per lane per chunk
 
@@ -63,7 +107,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
                                                          int64_t out_ph, int32_t* num_out,
                                                          uint64_t* desc) {
   using T = typename Bits<EB>::T;
-  constexpr int E = 16 / EB;                      // elements per 16-byte vector
+  constexpr int E = sel_e<EB>();                  // elements per payload vector
+  constexpr int VB = E * EB;                      // bytes per payload vector
+  using V = typename SelVec<VB>::T;
   constexpr int J = kSelJ;
   constexpr int64_t kChunkVecs = (int64_t)kWave * J;
   constexpr int64_t kWaveVecs = kChunkVecs * C;
@@ -107,6 +153,9 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     } else if constexpr (FVEC && E == 2) {
       (void)e0;
       return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(fb.r, u * 2, 0, kNT);
+    } else if constexpr (E == 1) {
+      (void)e0;     // one flag per vector: every loaded vector's element is live
+      return (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(fb.r, u, 0, kNT);
     } else {
       uint32_t f = 0u;
 #pragma unroll
@@ -125,7 +174,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   // jv the first vector of its load (wave-uniform) and `full` telling that
   // every element of the wave's run is live, elements outside [lo, hi) are
   // cleared only on the slow path.
-  constexpr uint32_t kTop = E == 4 ? 0x80808080u : 0x8080u;   // bit 7 of each flag byte
+  constexpr uint32_t kTop = E == 4 ? 0x80808080u : (E == 2 ? 0x8080u : 0x80u);   // bit 7 of each flag byte
   auto sel_bits = [&](int64_t jv, uint32_t f, bool full) {
     uint32_t t = (((f & 0x7f7f7f7fu) + 0x7f7f7f7fu) | f) & kTop;
     if (!full && !(jv * E >= lo && (jv + kWave) * E <= hi)) {   // wave-uniform
@@ -149,15 +198,14 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   // sb[c]: selection bits of chunk c; element k of the lane's vector j is
   // selected when bit 8k + 7 - j is set
   uint32_t sb[C];
-  u32x4 pay[C][J];         // payload (only the chunks in flight are live)
-  const Buf pbuf = run_buf(in_base, 16, wb, kWaveVecs);
+  V pay[C][J];             // payload (only the chunks in flight are live)
+  const Buf pbuf = run_buf(in_base, VB, wb, kWaveVecs);
   auto load_chunk = [&](int c) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const uint32_t off = (uint32_t)(((c * J + j) * kWave + lane) * 16);
+      const uint32_t off = (uint32_t)(((c * J + j) * kWave + lane) * VB);
       const bool any = (sb[c] & (kTop >> j)) != 0u;
-      pay[c][j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(pbuf.r, any ? off : kOffNone, 0, kNT));
+      pay[c][j] = sel_load<VB>(pbuf.r, any ? off : kOffNone);
     }
   };
 
@@ -258,13 +306,21 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     // pack: selected elements to their slots, the others to the discard slot
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const u32x4 r = pay[c][j];
+      const V r = pay[c][j];
       T x[E];
-      if constexpr (EB == 4) {
+      if constexpr (EB == 1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = (uint8_t)(r >> (8 * k));
+      } else if constexpr (EB == 2) {
+        x[0] = (uint16_t)r.x; x[1] = (uint16_t)(r.x >> 16);
+        x[2] = (uint16_t)r.y; x[3] = (uint16_t)(r.y >> 16);
+      } else if constexpr (EB == 4) {
         x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
-      } else {
+      } else if constexpr (EB == 8) {
         x[0] = ((uint64_t)r.y << 32) | r.x;
         x[1] = ((uint64_t)r.w << 32) | r.z;
+      } else {
+        x[0] = r;
       }
       uint32_t p = pos[j];
 #pragma unroll
@@ -280,15 +336,14 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     // store stage vectors [0, nvec) to output vectors g0 + q
     const int64_t g0 = ((int64_t)r0 + out_ph) / E;
     const int nvec = (end + E - 1) / E;
-    const Buf ob(out_base + g0 * 16, (int64_t)nvec * 16);
+    const Buf ob(out_base + g0 * VB, (int64_t)nvec * VB);
 #pragma unroll
     for (int i = 0; i < kStoreIters; ++i) {
       const int q = lane + i * kWave;
       const bool full = q * E >= s && (q + 1) * E <= end;
       const int qr = q < kStageVecs ? q : kStageVecs - 1;
-      const u32x4 v = *(const u32x4*)&stage[qr * E];
-      __builtin_amdgcn_raw_buffer_store_b128(v, ob.r, full ? (uint32_t)(q * 16) : kOffNone, 0,
-                                             kStoreAux);
+      const V v = *(const V*)&stage[qr * E];
+      sel_store<VB>(v, ob.r, full ? (uint32_t)(q * VB) : kOffNone);
     }
     // the partial vectors: the first (lane 0) and the last (lane 1), element by element
     {
@@ -301,12 +356,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
         const bool ok = partial && slot >= s && slot < end;
         const T v = stage[ok ? slot : 0];
         const uint32_t off = ok ? (uint32_t)(slot * EB) : kOffNone;
-        if constexpr (EB == 4) {
-          __builtin_amdgcn_raw_buffer_store_b32(v, ob.r, off, 0, kStoreAux);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ob.r, off, 0,
-                                                kStoreAux);
-        }
+        sel_store<EB>(v, ob.r, off);
       }
     }
     r0 += (uint32_t)(end - s);
@@ -320,11 +370,12 @@ static int64_t sel_tiles_for(int64_t n, int e, int64_t tv) {
   return v_last / tv + 1;
 }
 
-// Sized for 8-byte elements (two per vector, the most tiles) and the smallest
-// tile, so one scratch size serves both element widths and every launch shape.
+// Sized for 16-byte elements (one per vector, the most tiles) and the
+// smallest tile, so one scratch size serves every element width and launch
+// shape.
 size_t select_tiles(int64_t n, size_t elem_bytes) {
   (void)elem_bytes;
-  return (size_t)sel_tiles_for(n, 2, kSelMinTileVecs);
+  return (size_t)sel_tiles_for(n, 1, kSelMinTileVecs);
 }
 
 __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
@@ -335,11 +386,11 @@ template <int EB, int WD, int C>
 static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out, int32_t* num_out,
                                  int64_t n, void* scratch, hipStream_t stream,
                                  const int32_t* n_dev) {
-  constexpr int E = 16 / EB;
+  constexpr int E = sel_e<EB>(), VB = E * EB;
   constexpr int64_t TV = (int64_t)kWave * kSelJ * C * WD;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
-  const int64_t ph = (int64_t)((ia % 16) / EB);
-  const int64_t out_ph = (int64_t)((oa % 16) / EB);
+  const int64_t ph = (int64_t)((ia % VB) / EB);
+  const int64_t out_ph = (int64_t)((oa % VB) / EB);
   const uintptr_t fbase = fa - (uintptr_t)ph;          // flag byte of window element 0
   const bool fvec = (fbase % E) == 0;
   const int64_t ntiles = sel_tiles_for(n, E, TV);
@@ -372,8 +423,13 @@ hipError_t launch_select(const void* in, const uint8_t* flags, void* out, int32_
     store_count_zero_kernel<<<dim3(1), dim3(1), 0, stream>>>(num_out);
     return hipGetLastError();
   }
-  if (elem_bytes == 4) return launch_sel_t<4>(in, flags, out, num_out, n, scratch, stream, n_dev);
-  return launch_sel_t<8>(in, flags, out, num_out, n, scratch, stream, n_dev);
+  switch (elem_bytes) {
+    case 1: return launch_sel_t<1>(in, flags, out, num_out, n, scratch, stream, n_dev);
+    case 2: return launch_sel_t<2>(in, flags, out, num_out, n, scratch, stream, n_dev);
+    case 4: return launch_sel_t<4>(in, flags, out, num_out, n, scratch, stream, n_dev);
+    case 8: return launch_sel_t<8>(in, flags, out, num_out, n, scratch, stream, n_dev);
+    default: return launch_sel_t<16>(in, flags, out, num_out, n, scratch, stream, n_dev);
+  }
 }
 
 }  // namespace sca

@@ -158,8 +158,10 @@ def test_select_validation():
     L = sc.lib()
     need = L.select_compact_scratch_bytes(1000)
     N = B + 0x100000
-    assert L.select_compact(A, S + 0x1000, B, N, 1000, 2, S, need, None) == ENOTSUP
-    assert L.select_compact(A, S + 0x1000, B, N, 1000, 16, S, need, None) == ENOTSUP
+    for eb in (0, 3, 5, 12, 32):                     # element widths other than 1/2/4/8/16
+        assert L.select_compact(A, S + 0x1000, B, N, 1000, eb, S, need, None) == ENOTSUP
+    assert L.select_compact(A + 1, S + 0x1000, B, N, 1000, 2, S, need, None) == EINVAL   # in alignment
+    assert L.select_compact(A, S + 0x1000, B + 8, N, 1000, 16, S, need, None) == EINVAL  # out alignment
     assert L.select_compact(A, S + 0x1000, B, None, 1000, 4, S, need, None) == EINVAL
     assert L.select_compact(A, S + 0x1000, B, N + 2, 1000, 4, S, need, None) == EINVAL
     assert L.select_compact(A, S + 0x10000, B, N, -5, 4, S, need, None) == EINVAL

@@ -248,36 +248,74 @@ def test_device_signed_zero_and_inf():
 
 SEL_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 8191, 8192, 8193,
              20_000, 1_000_003]
-SENTINEL = {4: 0x5A5A5A5A, 8: 0x5A5A5A5A5A5A5A5A}
+SENTINEL_BYTE = 0x5A
+# torch dtypes that carry elements of each width bit for bit (16 bytes: complex128)
+SEL_NP = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64, 16: np.complex128}
+SEL_EB = [1, 2, 4, 8, 16]
 
 
 def run_select(x, flags, eb, label):
-    n = x.size
-    xd = torch.from_numpy(x.view(np.int32 if eb == 4 else np.int64).copy()).cuda()
+    """x: numpy array of n elements of eb bytes (any dtype of that width).
+    Compares bytes with the oracle and checks that nothing past the count was
+    written."""
+    n = x.shape[0]
+    xb = np.ascontiguousarray(x).view(np.uint8).reshape(n, eb)
+    xd = torch.from_numpy(xb.reshape(-1).view(SEL_NP[eb]).copy()).cuda()
     fd = torch.from_numpy(flags.copy()).cuda()
-    out = torch.full((n,), SENTINEL[eb], dtype=xd.dtype, device="cuda")
+    out = torch.from_numpy(np.full(n * eb, SENTINEL_BYTE, np.uint8).view(SEL_NP[eb])).cuda()
     out, num = sc.select_compact(xd, fd, out=out)
     torch.cuda.synchronize()
     k = int(num.item())
-    ora, ko = oracle.select(x, flags)
+    ora, ko = oracle.select(xb.reshape(-1).view(np.dtype((np.void, eb))), flags)
     assert k == ko, f"{label}: count {k} != {ko}"
-    got = out.cpu().numpy().view(x.dtype)
-    check_exact(got[:k], ora[:k], label)
-    tail = out.cpu().numpy()[k:]
-    assert (tail.view(np.uint32 if eb == 4 else np.uint64) == SENTINEL[eb]).all(), \
-        f"{label}: tail written"
+    got = out.cpu().numpy().view(np.uint8).reshape(n, eb)
+    want = np.ascontiguousarray(ora).view(np.uint8).reshape(n, eb)
+    check_exact(got[:k].reshape(-1), want[:k].reshape(-1), label)
+    assert (got[k:] == SENTINEL_BYTE).all(), f"{label}: tail written"
     return k
 
 
-@pytest.mark.parametrize("eb", [4, 8])
+def sel_payload(n, eb, seed):
+    """n elements of eb random bytes each (uint8 matrix viewed as one row per element)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, size=(n, eb), dtype=np.uint8).reshape(-1).view(
+        np.dtype((np.void, eb)))
+
+
+@pytest.mark.parametrize("eb", SEL_EB)
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.5, 0.99, 1.0])
 def test_select_sizes(eb, p):
     for i, n in enumerate(SEL_SIZES):
-        rng = np.random.default_rng(3000 + i)
-        x = rng.integers(0, 1 << 62, size=n, dtype=np.int64)
-        x = x.astype(np.uint32) if eb == 4 else x.astype(np.uint64)
+        x = sel_payload(n, eb, 3000 + i)
         flags = workloads.bernoulli_flags(n, p, 4000 + i)
         run_select(x, flags, eb, f"select eb={eb} p={p} n={n}")
+
+
+@pytest.mark.parametrize("eb", [1, 2, 8, 16])
+def test_select_misaligned_views_all_widths(eb):
+    # element offsets move payload, flags and output off their vector
+    # alignment (4, 8 or 16 bytes), with equal and unequal phases
+    n = 30_011
+    xb = np.ascontiguousarray(sel_payload(n, eb, 11)).view(np.uint8).reshape(n, eb)
+    flags = workloads.bernoulli_flags(n, 0.5, 12)
+    ora, ko = oracle.select(xb.reshape(-1).view(np.dtype((np.void, eb))), flags)
+    want = np.ascontiguousarray(ora).view(np.uint8).reshape(n, eb)
+    dt = SEL_NP[eb]
+    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1)):
+        big_in = torch.zeros(n + 8, dtype=torch.from_numpy(np.zeros(1, dt)).dtype, device="cuda")
+        big_f = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+        fill = np.full((n + 8) * eb, 7, np.uint8).view(dt)
+        big_out = torch.from_numpy(fill).cuda()
+        big_in[off_in:off_in + n].copy_(torch.from_numpy(xb.reshape(-1).view(dt).copy()).cuda())
+        big_f[off_f:off_f + n].copy_(torch.from_numpy(flags).cuda())
+        _, num = sc.select_compact(big_in[off_in:off_in + n], big_f[off_f:off_f + n],
+                                   out=big_out[off_out:off_out + n])
+        k = int(num.item())
+        assert k == ko
+        got = big_out.cpu().numpy().view(np.uint8).reshape(n + 8, eb)
+        label = f"select eb={eb} offsets {off_in},{off_f},{off_out}"
+        check_exact(got[off_out:off_out + k].reshape(-1), want[:k].reshape(-1), label)
+        assert (got[:off_out] == 7).all() and (got[off_out + k:] == 7).all(), label
 
 
 @pytest.mark.parametrize("p", workloads.SELECT_P)
