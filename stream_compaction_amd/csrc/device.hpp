@@ -391,14 +391,14 @@ struct VecIO {
 
 // ---------------------------------------------------------------------------
 // Tile descriptors for decoupled look-back.  Every descriptor word is one
-// 64-bit value written once per call with a single relaxed agent-scope atomic
-// store and read with relaxed agent-scope atomic loads, which on gfx950 are
-// coherent across the XCDs' separate L2 caches.  Because a status and the
-// value it qualifies always travel in the same word, no fence orders them.
-//  - 32-bit values: one word  (status << 32) | value.
+// 64-bit value written once per call and read with the cache policy of
+// relaxed agent-scope atomics (sc1), which on gfx950 is coherent across the
+// XCDs' separate L2 caches.  Because a status and the value it qualifies
+// always travel in the same word, no fence orders them.
+//  - 32-bit values: one word  (status << 32) | value, one atomic store.
 //  - 64-bit values: four words (aggregate lo/hi, inclusive lo/hi), each
-//    (1 << 32) | half; a reader accepts a slot only when both halves are
-//    present, so it never mixes the two slots.
+//    (1 << 32) | half, a pair written by one 16-byte store; a reader accepts
+//    a pair only when both halves are present, so it never mixes the two.
 // Status: 0 = nothing yet, 1 = tile aggregate, 2 = inclusive prefix.
 // A zero-filled descriptor array is the initial state.
 // ---------------------------------------------------------------------------
