@@ -128,6 +128,33 @@ def test_select_devn():
     replay_each(capture, check)
 
 
+@pytest.mark.parametrize("eb,tdt", [(1, torch.uint8), (2, torch.int16), (16, torch.complex128)])
+def test_select_devn_widths(eb, tdt):
+    # elements of 1, 2 and 16 bytes; compared byte for byte, tail untouched
+    rng = np.random.default_rng(25 + eb)
+    xb = rng.integers(0, 256, size=(CAP, eb), dtype=np.uint8)
+    f = (rng.random(CAP) < 0.4).astype(np.uint8)
+    npdt = {1: np.uint8, 2: np.int16, 16: np.complex128}[eb]
+    xd = torch.from_numpy(xb.reshape(-1).view(npdt).copy()).cuda()
+    fd = torch.from_numpy(f).cuda()
+    out = torch.from_numpy(np.full(CAP * eb, 7, np.uint8).view(npdt)).cuda()
+    assert xd.dtype == tdt
+    num = torch.empty(1, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(sc.select_compact_scratch_bytes(CAP), dtype=torch.uint8, device="cuda")
+    xv = xb.reshape(-1).view(np.dtype((np.void, eb)))
+
+    def capture(n_live):
+        sc.select_compact(xd, fd, out=out, num_out=num, scratch=scratch, n_live=n_live)
+
+    def check(n, c):
+        o, k = oracle.select(xv[:n], f[:n])
+        assert int(num.item()) == k, (c, k)
+        got = out.cpu().numpy().view(np.uint8).reshape(CAP, eb)
+        want = np.ascontiguousarray(o).view(np.uint8).reshape(n, eb)
+        check_exact(got[:k].reshape(-1), want[:k].reshape(-1), f"select_devn eb={eb} count {c}")
+    replay_each(capture, check)
+
+
 def test_reduce_by_key_devn():
     rng = np.random.default_rng(24)
     keys = np.repeat(rng.integers(0, 5, size=CAP), rng.geometric(0.2, size=CAP))[:CAP]
