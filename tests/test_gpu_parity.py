@@ -53,6 +53,18 @@ def test_rows_shapes(dt, op, excl):
         compare_scan(from_dev(out, dt), x, dt, op, excl, label)
 
 
+@pytest.mark.parametrize("rows,n", [(1 << 20, 1), (1 << 20, 3), (65_537, 2)])
+def test_rows_many_tiny_rows(rows, n):
+    # about a million one-wave workgroups, each row within one partial vector
+    for dt in ("f32", "bf16"):
+        x = rand_input(dt, (rows, n), 1500 + n)
+        for op, excl in (("add", True), ("max", False), ("min", True)):
+            out = sc.scan_rows(to_dev(x, dt), op=op, exclusive=excl)
+            torch.cuda.synchronize()
+            compare_scan(from_dev(out, dt), x, dt, op, excl,
+                         f"scan_rows {dt} {op} excl={excl} [{rows},{n}]")
+
+
 def test_rows_workload1_full():
     rows, n = workloads.FULL["rows_f32"]
     x = workloads.rows_f32(rows, n)
