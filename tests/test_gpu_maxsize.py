@@ -1,4 +1,5 @@
-"""Every entry point at the largest count the C ABI accepts, n = 2^31 - 1.
+"""Every entry point at the largest count the C ABI accepts, n = 2^31 - 1,
+and a row scan whose rows together pass 2^31 elements.
 
 At this size the checks are closed forms of the inputs, evaluated with torch
 on the GPU (no call into this library), chunk by chunk:
@@ -90,6 +91,22 @@ def test_scan_rows_one_max_row():
     for a, b in chunks(N):
         want = (torch.arange(a, b, dtype=torch.int32, device="cuda") % 2).to(torch.bfloat16)
         assert torch.equal(out[0, a:b], want), f"elements [{a}, {b})"
+
+
+def test_scan_rows_past_2_31_elements():
+    # 65,537 rows of 32,771 elements: 2^31 + 2^16 + ... elements in all, so row
+    # offsets pass 32 bits; rows of odd length start inside 16-byte vectors
+    rows, n = 65_537, 32_771
+    note(f"scan_rows bf16 [{rows}, {n}] exclusive add")
+    i = torch.arange(n, dtype=torch.int32, device="cuda")
+    row = (1 - 2 * (i % 2)).to(torch.bfloat16)
+    x = row.expand(rows, n).contiguous()
+    out = sc.scan_rows(x, op="add", exclusive=True)
+    torch.cuda.synchronize()
+    want = (i % 2).to(torch.bfloat16)
+    for r0 in range(0, rows, 8192):
+        r1 = min(rows, r0 + 8192)
+        assert torch.equal(out[r0:r1], want.expand(r1 - r0, n)), f"rows [{r0}, {r1})"
 
 
 def test_reduce_by_key_max_count():
