@@ -129,6 +129,17 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
 template <int VB> struct ValBits { using T = uint32_t; };
 template <> struct ValBits<8> { using T = uint64_t; };
 
+// The half-wave ranking (below) serves keys-only sorts, where its lower
+// register count lets more workgroups share a CU: 2.78 against 3.06 ms for
+// 2^28 u32 keys.  With 4-byte values (one 16-wave workgroup per CU either
+// way) its doubled instructions cost more than they save: 5.36-5.41 against
+// 5.24 ms.  SCA_RX_HALF_ALL=1 selects it for every value width.
+#ifndef SCA_RX_HALF_ALL
+#define SCA_RX_HALF_ALL 0
+#endif
+template <int VB>
+constexpr bool rx_half_rank() { return SCA_RX_HALF_ALL || VB == 0; }
+
 // A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
 // 32-bit, and accesses past the range read zero or are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rx_rsrc(const void* base, uint64_t bytes) {
@@ -153,17 +164,20 @@ __device__ __forceinline__ void rx_store(__amdgpu_buffer_rsrc_t r, uint32_t off,
 }
 
 // Ranking.  For each load, the lanes holding the same digit are found through
-// a per-wave LDS table of 64-bit lane masks, one entry per digit (and one for
-// "no key"): every lane ORs its lane bit into its digit's entry, reads the
-// entry back and clears it.  LDS work from one wave is carried out in issue
-// order, so the read sees the OR of every lane and the next load's ORs come
-// after the clear.  A lane's rank is the count of such lanes below it plus the
-// wave's running count of the digit, so ranks follow input order.
+// a per-wave LDS table, one 64-bit entry per digit (and one for "no key"):
+// the lanes of a half-wave OR their bit into the entry's low word, read the
+// entry back and write it with the mask cleared and the high word, the
+// wave's running count of the digit, advanced.  LDS work from one wave is
+// carried out in issue order, so a read sees the OR of every lane of its half
+// and the next half's or load's ORs come after the write.  A lane's rank is
+// the count of matching lanes below it in its half plus the running count, so
+// ranks follow input order.
 //
 // Stores: with B32 the outputs are written through buffer resources with
 // 32-bit byte offsets (every array below 4 GiB); else through 64-bit
 // addresses.  FULL tiles skip every per-key range test.
-template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL>
+template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL,
+          bool HALF = rx_half_rank<VB>()>
 __device__ __forceinline__ void rx_scatter_tile(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
     void* __restrict__ vout_, int64_t n, int shift, int64_t t0, int count,
@@ -197,21 +211,55 @@ __device__ __forceinline__ void rx_scatter_tile(
   }
 
   // ---- rank within the wave ----
+  // Each table entry holds, in its low word, the lane mask of one half-wave
+  // for the current load and, in its high word, the wave's running count of
+  // the digit.  The lower half of the wave goes first: its lanes OR in their
+  // bits, read the entry (mask and count), and write back a clear mask with
+  // the count advanced; the upper half then does the same and so sees the
+  // lower half's keys counted, which keeps ranks in input order.
   uint32_t* cnt = s_wcnt[wave];
-  const uint64_t lbit = 1ull << lane;
+  if constexpr (!HALF) {
+    // full-wave form: the whole wave's mask in the entry, the running count
+    // in s_wcnt
+    const uint64_t lbit = 1ull << lane;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+    for (int j = 0; j < KPT; ++j) {
+      uint64_t* e = s_tab + dg[j];
+      __hip_atomic_fetch_or(e, lbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint64_t match = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t old = __hip_atomic_load(cnt + dg[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0u));
+      const uint32_t same = (uint32_t)__builtin_popcountll(match);
+      // every lane of the digit writes the same new count
+      __hip_atomic_store(cnt + dg[j], old + same, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      rank[j] = old + below;
+    }
+  }
+  const uint32_t hbit = 1u << (lane & 31);
+#pragma unroll
+  for (int j = 0; j < (HALF ? KPT : 0); ++j) {
     uint64_t* e = s_tab + dg[j];
-    __hip_atomic_fetch_or(e, lbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint64_t match = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t old = __hip_atomic_load(cnt + dg[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_store(e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0u));
-    const uint32_t same = (uint32_t)__builtin_popcountll(match);
-    // every lane of the digit writes the same new count
-    __hip_atomic_store(cnt + dg[j], old + same, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    rank[j] = old + below;
+    uint32_t r = 0u;
+    if (lane < 32) {
+      __hip_atomic_fetch_or((uint32_t*)e, hbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint64_t t = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t m = (uint32_t)t, c = (uint32_t)(t >> 32);
+      // every lane of the digit writes the same entry
+      __hip_atomic_store(e, (uint64_t)(c + (uint32_t)__builtin_popcount(m)) << 32,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      r = c + __builtin_amdgcn_mbcnt_lo(m, 0u);
+    }
+    if (lane >= 32) {
+      __hip_atomic_fetch_or((uint32_t*)e, hbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint64_t t = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t m = (uint32_t)t, c = (uint32_t)(t >> 32);
+      __hip_atomic_store(e, (uint64_t)(c + (uint32_t)__builtin_popcount(m)) << 32,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      r = c + __builtin_amdgcn_mbcnt_hi(m, 0u);
+    }
+    rank[j] = r;
   }
   __syncthreads();
 
@@ -220,7 +268,8 @@ __device__ __forceinline__ void rx_scatter_tile(
     uint32_t h = 0u;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      const uint32_t c = s_wcnt[w][tid];
+      const uint32_t c = HALF ? (uint32_t)(((const uint64_t*)s_buf)[w * kBins1 + tid] >> 32)
+                              : s_wcnt[w][tid];
       s_wcnt[w][tid] = h;
       h += c;
     }
