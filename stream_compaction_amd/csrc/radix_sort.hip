@@ -176,12 +176,12 @@ __device__ __forceinline__ void rx_store(__amdgpu_buffer_rsrc_t r, uint32_t off,
 // Stores: with B32 the outputs are written through buffer resources with
 // 32-bit byte offsets (every array below 4 GiB); else through 64-bit
 // addresses.  FULL tiles skip every per-key range test.
-template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL,
+template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL, class WC,
           bool HALF = rx_half_rank<VB>()>
 __device__ __forceinline__ void rx_scatter_tile(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
     void* __restrict__ vout_, int64_t n, int shift, int64_t t0, int count,
-    uint32_t (*s_wcnt)[kRxBins + 1], uint32_t* s_start, uint32_t* s_g, uint32_t* s_sum,
+    WC (*s_wcnt)[kRxBins + 1], uint32_t* s_start, uint32_t* s_g, uint32_t* s_sum,
     unsigned char* s_buf) {
   using VT = typename ValBits<VB>::T;
   constexpr int kThreads = 64 * WAVES;
@@ -217,7 +217,7 @@ __device__ __forceinline__ void rx_scatter_tile(
   // bits, read the entry (mask and count), and write back a clear mask with
   // the count advanced; the upper half then does the same and so sees the
   // lower half's keys counted, which keeps ranks in input order.
-  uint32_t* cnt = s_wcnt[wave];
+  WC* cnt = s_wcnt[wave];
   if constexpr (!HALF) {
     // full-wave form: the whole wave's mask in the entry, the running count
     // in s_wcnt
@@ -270,7 +270,7 @@ __device__ __forceinline__ void rx_scatter_tile(
     for (int w = 0; w < WAVES; ++w) {
       const uint32_t c = HALF ? (uint32_t)(((const uint64_t*)s_buf)[w * kBins1 + tid] >> 32)
                               : s_wcnt[w][tid];
-      s_wcnt[w][tid] = h;
+      s_wcnt[w][tid] = (WC)h;
       h += c;
     }
     const uint32_t incl = wave_scan_incl<Op::Add>(h);
@@ -284,7 +284,7 @@ __device__ __forceinline__ void rx_scatter_tile(
     const uint32_t st = s_start[tid] + off;           // the digit's first slot in the tile
     s_g[tid] -= st;                                   // its output position minus that slot
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s_wcnt[w][tid] += st;
+    for (int w = 0; w < WAVES; ++w) s_wcnt[w][tid] = (WC)(s_wcnt[w][tid] + st);
   }
   __syncthreads();
 
@@ -292,7 +292,7 @@ __device__ __forceinline__ void rx_scatter_tile(
   int lpos[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    lpos[j] = (int)(cnt[dg[j]] + rank[j]);
+    lpos[j] = (int)((uint32_t)cnt[dg[j]] + rank[j]);
     if (FULL || dg[j] < (uint32_t)kRxBins) s_keys[lpos[j]] = k[j];
   }
   __syncthreads();
@@ -349,17 +349,26 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
   constexpr int kBins1 = kRxBins + 1;
+  constexpr bool kHalf = rx_half_rank<VB>();
   constexpr int kSortBytes = kTile * (int)(sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB);
   constexpr int kTabBytes = WAVES * kBins1 * 8;
-  constexpr int kBufBytes = kSortBytes > kTabBytes ? kSortBytes : kTabBytes;
+  // the digits' first slots sit past the tables until the reorder
+  constexpr int kTabStartBytes = kTabBytes + kRxBins * 4;
+  constexpr int kBufBytes = kSortBytes > kTabStartBytes ? kSortBytes : kTabStartBytes;
   static_assert(kThreads >= kRxBins, "one thread per digit");
-  __shared__ uint32_t s_wcnt[WAVES][kBins1];    // per wave: running count, then first slot
-  __shared__ uint32_t s_start[kRxBins];         // the digit's first slot in the tile
+  // With the half-wave ranking the running counts live in the tables, and
+  // this array only holds each wave's first slot per digit, below the tile
+  // size: 16 bits, which keeps a keys-only workgroup under a quarter of the
+  // CU's LDS (four resident instead of three).
+  using WC = std::conditional_t<kHalf, uint16_t, uint32_t>;
+  static_assert(!kHalf || kTile < 65536, "first slots fit 16 bits");
+  __shared__ WC s_wcnt[WAVES][kBins1];          // per wave: running count, then first slot
   __shared__ uint32_t s_g[kRxBins];             // the digit's first output position (then
                                                 // that minus its first slot in the tile)
   __shared__ uint32_t s_sum[kRxBins / 64];
   // lane-mask tables while ranking, then the tile reordered by digit
   __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
+  uint32_t* s_start = (uint32_t*)(s_buf + kTabBytes);   // the digit's first slot in the tile
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int64_t tile = rx_xcd_tile(blockIdx.x, ntiles);
@@ -367,7 +376,9 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   const int64_t n = live_count(n_cap, n_dev);
   const int count =                                  // keys in this tile
       (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
-  for (int i = tid; i < WAVES * kBins1; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
+  if constexpr (!kHalf) {
+    for (int i = tid; i < WAVES * kBins1; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
+  }
   uint64_t* tab = (uint64_t*)s_buf + wave * kBins1;
   for (int i = lane; i < kBins1; i += kWave) tab[i] = 0ull;
   if (tid < kRxBins) s_g[tid] = offsets[(int64_t)tid * ntiles + tile];
