@@ -129,16 +129,26 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
 template <int VB> struct ValBits { using T = uint32_t; };
 template <> struct ValBits<8> { using T = uint64_t; };
 
-// The half-wave ranking (below) serves keys-only sorts, where its lower
-// register count lets more workgroups share a CU: 2.78 against 3.06 ms for
-// 2^28 u32 keys.  With 4-byte values (one 16-wave workgroup per CU either
-// way) its doubled instructions cost more than they save: 5.36-5.41 against
-// 5.24 ms.  SCA_RX_HALF_ALL=1 selects it for every value width.
+// The half-wave ranking (below) takes fewer registers than the full-wave one
+// but twice its LDS instructions, so it pays where the registers it frees let
+// more workgroups share a CU.  Keys only: 2.78 against 3.06 ms for 2^28 u32
+// keys.  32-bit keys with 4-byte values: the values are loaded after the
+// ranking and the positions held packed (below), which brings the 16-wave
+// workgroup to 57 VGPRs and two workgroups per CU: 4.64 against 5.22 ms for
+// 2^28 pairs (with the values held through the ranking instead, one
+// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).
+// SCA_RX_HALF_ALL=1 selects it for every key and value width.
 #ifndef SCA_RX_HALF_ALL
 #define SCA_RX_HALF_ALL 0
 #endif
-template <int VB>
-constexpr bool rx_half_rank() { return SCA_RX_HALF_ALL || VB == 0; }
+#ifndef SCA_RX_HALF_K64
+#define SCA_RX_HALF_K64 0
+#endif
+template <class KT, int VB>
+constexpr bool rx_half_rank() {
+  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4) ||
+         (SCA_RX_HALF_K64 && sizeof(KT) == 8);
+}
 
 // A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
 // 32-bit, and accesses past the range read zero or are dropped.
@@ -177,7 +187,7 @@ __device__ __forceinline__ void rx_store(__amdgpu_buffer_rsrc_t r, uint32_t off,
 // 32-bit byte offsets (every array below 4 GiB); else through 64-bit
 // addresses.  FULL tiles skip every per-key range test.
 template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL, class WC,
-          bool HALF = rx_half_rank<VB>()>
+          bool HALF = rx_half_rank<KT, VB>()>
 __device__ __forceinline__ void rx_scatter_tile(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
     void* __restrict__ vout_, int64_t n, int shift, int64_t t0, int count,
@@ -191,6 +201,12 @@ __device__ __forceinline__ void rx_scatter_tile(
   uint64_t* s_tab = (uint64_t*)s_buf + wave_id() * kBins1;   // this wave's lane-mask table
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
 
+  // With values and the half-wave ranking, the values are loaded only once
+  // the keys are ranked, and ranks, reorder positions and output digits are
+  // held packed (two or four to a register), which brings a 16-wave
+  // workgroup to at most 64 VGPRs.
+  constexpr bool kLateV = HALF && VB != 0;
+
   // ---- load (buffer resources bounded at the tile's keys) ----
   const int wbase = wave * 64 * KPT;                 // the wave's first slot in the tile
   const auto kr = rx_rsrc(kin + t0, (uint64_t)count * sizeof(KT));
@@ -198,11 +214,18 @@ __device__ __forceinline__ void rx_scatter_tile(
   VT v[VB != 0 ? KPT : 1];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) k[j] = rx_load<KT>(kr, (uint32_t)((wbase + j * 64 + lane) * sizeof(KT)));
-  if constexpr (VB != 0) {
+  auto load_values = [&]() {
     const auto vr = rx_rsrc((const VT*)vin_ + t0, (uint64_t)count * VB);
+    // the lane's first offset, opaque to the compiler: the loads then take
+    // j * 64 * VB as their immediate offset instead of sixteen address
+    // registers computed ahead of time
+    uint32_t vo = (uint32_t)((wbase + lane) * VB);
+    if constexpr (kLateV) asm volatile("" : "+v"(vo));
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) v[j] = rx_load<VT>(vr, (uint32_t)((wbase + j * 64 + lane) * VB));
-  }
+    for (int j = 0; j < KPT; ++j) v[j] = rx_load<VT>(vr, vo + (uint32_t)(j * 64 * VB));
+  };
+  if constexpr (VB != 0 && !kLateV) load_values();
+  auto valid = [&](int j) { return FULL || wbase + j * 64 + lane < count; };
   uint32_t dg[KPT], rank[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -238,6 +261,7 @@ __device__ __forceinline__ void rx_scatter_tile(
     }
   }
   const uint32_t hbit = 1u << (lane & 31);
+  uint32_t rpk[(KPT + 1) / 2] = {};                  // ranks, two 16-bit halves a register
 #pragma unroll
   for (int j = 0; j < (HALF ? KPT : 0); ++j) {
     uint64_t* e = s_tab + dg[j];
@@ -259,7 +283,11 @@ __device__ __forceinline__ void rx_scatter_tile(
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       r = c + __builtin_amdgcn_mbcnt_hi(m, 0u);
     }
-    rank[j] = r;
+    if constexpr (kLateV) {
+      rpk[j >> 1] |= r << ((j & 1) * 16);            // below the tile size
+    } else {
+      rank[j] = r;
+    }
   }
   __syncthreads();
 
@@ -289,11 +317,26 @@ __device__ __forceinline__ void rx_scatter_tile(
   __syncthreads();
 
   // ---- reorder by digit in LDS (the tables are no longer needed) ----
+  if constexpr (kLateV) load_values();             // in flight while the keys move
   int lpos[KPT];
+  uint32_t lpk[(KPT + 1) / 2] = {};                  // kLateV: positions, two a register
+  // kLateV: the shift made opaque here, so the digits are computed again from
+  // the keys rather than held across the barriers
+  int sh = shift;
+  if constexpr (kLateV) asm volatile("" : "+s"(sh));
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    lpos[j] = (int)((uint32_t)cnt[dg[j]] + rank[j]);
-    if (FULL || dg[j] < (uint32_t)kRxBins) s_keys[lpos[j]] = k[j];
+    if constexpr (kLateV) {
+      // the digit again from the key, the rank from its packed half
+      const uint32_t d = valid(j) ? (uint32_t)((sort_image<KT, KK>(k[j]) >> sh) & 255u)
+                                  : (uint32_t)kRxBins;
+      const uint32_t p = (uint32_t)cnt[d] + ((rpk[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
+      lpk[j >> 1] |= (p & 0xffffu) << ((j & 1) * 16);
+      if (valid(j)) s_keys[p] = k[j];
+    } else {
+      lpos[j] = (int)((uint32_t)cnt[dg[j]] + rank[j]);
+      if (FULL || dg[j] < (uint32_t)kRxBins) s_keys[lpos[j]] = k[j];
+    }
   }
   __syncthreads();
 
@@ -302,6 +345,7 @@ __device__ __forceinline__ void rx_scatter_tile(
   // store inside the output whatever the input)
   const auto okr = rx_rsrc(kout, B32 ? (uint64_t)n * sizeof(KT) : 0);
   uint32_t dst[KPT];
+  uint32_t dpk[(KPT + 3) / 4] = {};                  // kLateV: each slot's digit, four a register
 #pragma unroll
   for (int m = 0; m < KPT; ++m) {
     const int slot = tid + m * kThreads;
@@ -310,19 +354,37 @@ __device__ __forceinline__ void rx_scatter_tile(
       const KT key = s_keys[slot];
       const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
       const uint32_t g = s_g[d] + (uint32_t)slot;     // modulo 2^32, like the offsets
-      dst[m] = g;
+      if constexpr (kLateV) {
+        dpk[m >> 2] |= d << ((m & 3) * 8);
+      } else {
+        dst[m] = g;
+      }
       if constexpr (B32) {
         rx_store<KT>(okr, g * (uint32_t)sizeof(KT), key);
       } else {
         if (g < (uint64_t)n) *gptr<KT>((uintptr_t)(kout + g)) = key;
       }
     }
+    // kLateV: at most four slots' reads in flight, which bounds the registers
+    if (kLateV && (m & 3) == 3) asm volatile("" ::: "memory");
   }
   if constexpr (VB != 0) {
     __syncthreads();                                   // every key is out of the buffer
+    if constexpr (kLateV) {
+      // opaque from here: unpacked only now, not kept unpacked through the key writes
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (FULL || dg[j] < (uint32_t)kRxBins) s_vals[lpos[j]] = v[j];
+      for (int i = 0; i < (KPT + 1) / 2; ++i) asm volatile("" : "+v"(lpk[i]));
+#pragma unroll
+      for (int i = 0; i < (KPT + 3) / 4; ++i) asm volatile("" : "+v"(dpk[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if constexpr (kLateV) {
+        if (valid(j)) s_vals[(lpk[j >> 1] >> ((j & 1) * 16)) & 0xffffu] = v[j];
+      } else {
+        if (FULL || dg[j] < (uint32_t)kRxBins) s_vals[lpos[j]] = v[j];
+      }
+    }
     __syncthreads();
     VT* vout = (VT*)vout_;
     const auto ovr = rx_rsrc(vout, B32 ? (uint64_t)n * VB : 0);
@@ -331,12 +393,15 @@ __device__ __forceinline__ void rx_scatter_tile(
       const int slot = tid + m * kThreads;
       if (FULL || slot < count) {
         const VT x = s_vals[slot];
+        const uint32_t g = kLateV ? s_g[(dpk[m >> 2] >> ((m & 3) * 8)) & 255u] + (uint32_t)slot
+                                  : dst[m];
         if constexpr (B32) {
-          rx_store<VT>(ovr, dst[m] * (uint32_t)VB, x);
+          rx_store<VT>(ovr, g * (uint32_t)VB, x);
         } else {
-          if (dst[m] < (uint64_t)n) *gptr<VT>((uintptr_t)(vout + dst[m])) = x;
+          if (g < (uint64_t)n) *gptr<VT>((uintptr_t)(vout + g)) = x;
         }
       }
+      if (kLateV && (m & 3) == 3) asm volatile("" ::: "memory");
     }
   }
 }
@@ -349,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
   constexpr int kBins1 = kRxBins + 1;
-  constexpr bool kHalf = rx_half_rank<VB>();
+  constexpr bool kHalf = rx_half_rank<KT, VB>();
   constexpr int kSortBytes = kTile * (int)(sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB);
   constexpr int kTabBytes = WAVES * kBins1 * 8;
   // the digits' first slots sit past the tables until the reorder
@@ -437,7 +502,8 @@ static hipError_t rx_copy(const void* src, void* dst, size_t bytes, hipStream_t 
 
 // Tile shape per key and value width.  32-bit keys alone: 8 waves x 16 keys
 // per thread (8192 keys).  32-bit keys with 4-byte values: 16 waves x 16
-// (16384 keys, one workgroup per CU by LDS): the longer digit runs halve the
+// (16384 keys; with the half-wave ranking, 57 VGPRs and 74,800 bytes of LDS,
+// two workgroups per CU): the longer digit runs halve the
 // write streams per key, which measured 7.40 ms against 8.79 ms for 2^28
 // key-value pairs, while costing the keys-only sort (5.31 ms against 4.19)
 // its occupancy.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys: 8
