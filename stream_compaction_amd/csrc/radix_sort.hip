@@ -136,18 +136,16 @@ template <> struct ValBits<8> { using T = uint64_t; };
 // ranking and the positions held packed (below), which brings the 16-wave
 // workgroup to 57 VGPRs and two workgroups per CU: 4.64 against 5.22 ms for
 // 2^28 pairs (with the values held through the ranking instead, one
-// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).
-// SCA_RX_HALF_ALL=1 selects it for every key and value width.
+// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).  With
+// 64-bit keys and values it lost too, though it raised the occupancy from 6
+// to 8 waves per SIMD: 2^27 u64 keys with 4- / 8-byte values 9.14 / 11.79 ms
+// against 8.31 / 10.69.  SCA_RX_HALF_ALL=1 selects it for every width.
 #ifndef SCA_RX_HALF_ALL
 #define SCA_RX_HALF_ALL 0
 #endif
-#ifndef SCA_RX_HALF_K64
-#define SCA_RX_HALF_K64 0
-#endif
 template <class KT, int VB>
 constexpr bool rx_half_rank() {
-  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4) ||
-         (SCA_RX_HALF_K64 && sizeof(KT) == 8);
+  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4);
 }
 
 // A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
@@ -506,7 +504,8 @@ static hipError_t rx_copy(const void* src, void* dst, size_t bytes, hipStream_t 
 // two workgroups per CU): the longer digit runs halve the
 // write streams per key, which measured 7.40 ms against 8.79 ms for 2^28
 // key-value pairs, while costing the keys-only sort (5.31 ms against 4.19)
-// its occupancy.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys: 8
+// its occupancy; with the half-wave ranking, 8 x 16 tiles measured 6.32 ms
+// against 4.66.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys: 8
 // waves x 8 (the LDS reorder buffer holds one tile of the wider of key and
 // value).
 template <class KT, int VB> struct RxShape { static constexpr int kWaves = 8, kKpt = 8; };
