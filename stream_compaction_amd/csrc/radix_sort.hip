@@ -201,8 +201,10 @@ __device__ __forceinline__ void rx_scatter_tile(
 
   // With values and the half-wave ranking, the values are loaded only once
   // the keys are ranked, and ranks, reorder positions and output digits are
-  // held packed (two or four to a register), which brings a 16-wave
-  // workgroup to at most 64 VGPRs.
+  // held packed (two or four to a register).  That brings the 16-wave
+  // workgroup of 32-bit keys with 4-byte values to 57 VGPRs with 32-bit store
+  // offsets (70 with 64-bit addresses, for arrays of 4 GiB and more), so two
+  // workgroups share a CU.
   constexpr bool kLateV = HALF && VB != 0;
 
   // ---- load (buffer resources bounded at the tile's keys) ----
