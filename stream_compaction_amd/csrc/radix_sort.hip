@@ -320,10 +320,15 @@ __device__ __forceinline__ void rx_scatter_tile(
   if constexpr (kLateV) load_values();             // in flight while the keys move
   int lpos[KPT];
   uint32_t lpk[(KPT + 1) / 2] = {};                  // kLateV: positions, two a register
-  // kLateV: the shift made opaque here, so the digits are computed again from
-  // the keys rather than held across the barriers
+  // kLateV: the shift and the keys made opaque here, so the digits (and the
+  // keys' sortable images) are computed again rather than held across the
+  // barriers
   int sh = shift;
-  if constexpr (kLateV) asm volatile("" : "+s"(sh));
+  if constexpr (kLateV) {
+    asm volatile("" : "+s"(sh));
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(k[j]));
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if constexpr (kLateV) {
@@ -365,8 +370,9 @@ __device__ __forceinline__ void rx_scatter_tile(
         if (g < (uint64_t)n) *gptr<KT>((uintptr_t)(kout + g)) = key;
       }
     }
-    // kLateV: at most four slots' reads in flight, which bounds the registers
-    if (kLateV && (m & 3) == 3) asm volatile("" ::: "memory");
+    // kLateV: at most four slots' reads in flight, and each word of digits
+    // packed as soon as it is whole, which bounds the registers
+    if (kLateV && (m & 3) == 3) asm volatile("" : "+v"(dpk[m >> 2]) : : "memory");
   }
   if constexpr (VB != 0) {
     __syncthreads();                                   // every key is out of the buffer
