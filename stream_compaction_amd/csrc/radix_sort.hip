@@ -136,16 +136,19 @@ template <> struct ValBits<8> { using T = uint64_t; };
 // ranking and the positions held packed (below), which brings the 16-wave
 // workgroup to 57 VGPRs and two workgroups per CU: 4.64 against 5.22 ms for
 // 2^28 pairs (with the values held through the ranking instead, one
-// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).  With
-// 64-bit keys and values it lost too, though it raised the occupancy from 6
-// to 8 waves per SIMD: 2^27 u64 keys with 4- / 8-byte values 9.14 / 11.79 ms
-// against 8.31 / 10.69.  SCA_RX_HALF_ALL=1 selects it for every width.
+// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).  64-bit
+// keys with values: on 8 x 8 tiles it lost (2^27 u64 keys with 4- / 8-byte
+// values 9.14 / 11.79 ms against 8.31 / 10.69), but on 16 x 8 tiles, two
+// workgroups per CU at 46 / 51 VGPRs, it wins: 7.60 / 9.61 ms against 8.28 /
+// 10.66.  It stays off for 32-bit keys with 8-byte values, whose 8 x 16 tiles
+// fit two workgroups per CU by LDS either way.  SCA_RX_HALF_ALL=1 selects it
+// for every width.
 #ifndef SCA_RX_HALF_ALL
 #define SCA_RX_HALF_ALL 0
 #endif
 template <class KT, int VB>
 constexpr bool rx_half_rank() {
-  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4);
+  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4) || sizeof(KT) == 8;
 }
 
 // A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
@@ -202,9 +205,8 @@ __device__ __forceinline__ void rx_scatter_tile(
   // With values and the half-wave ranking, the values are loaded only once
   // the keys are ranked, and ranks, reorder positions and output digits are
   // held packed (two or four to a register).  That brings the 16-wave
-  // workgroup of 32-bit keys with 4-byte values to 57 VGPRs with 32-bit store
-  // offsets (70 with 64-bit addresses, for arrays of 4 GiB and more), so two
-  // workgroups share a CU.
+  // workgroups of 32-bit keys with 4-byte values to 57-60 VGPRs and of
+  // 64-bit keys with values to 46-51, so two share a CU.
   constexpr bool kLateV = HALF && VB != 0;
 
   // ---- load (buffer resources bounded at the tile's keys) ----
@@ -513,13 +515,16 @@ static hipError_t rx_copy(const void* src, void* dst, size_t bytes, hipStream_t 
 // write streams per key, which measured 7.40 ms against 8.79 ms for 2^28
 // key-value pairs, while costing the keys-only sort (5.31 ms against 4.19)
 // its occupancy; with the half-wave ranking, 8 x 16 tiles measured 6.32 ms
-// against 4.66.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys: 8
-// waves x 8 (the LDS reorder buffer holds one tile of the wider of key and
-// value).
+// against 4.66.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys alone:
+// 8 waves x 8; with values, 16 x 8 (8192 keys, 74,800 bytes of LDS, two
+// workgroups per CU), for the same longer digit runs.  The LDS reorder buffer
+// holds one tile of the wider of key and value.
 template <class KT, int VB> struct RxShape { static constexpr int kWaves = 8, kKpt = 8; };
 template <> struct RxShape<uint32_t, 0> { static constexpr int kWaves = 8, kKpt = 16; };
 template <> struct RxShape<uint32_t, 4> { static constexpr int kWaves = 16, kKpt = 16; };
 template <> struct RxShape<uint32_t, 8> { static constexpr int kWaves = 8, kKpt = 16; };
+template <> struct RxShape<uint64_t, 4> { static constexpr int kWaves = 16, kKpt = 8; };
+template <> struct RxShape<uint64_t, 8> { static constexpr int kWaves = 16, kKpt = 8; };
 
 template <class KT, int VB>
 constexpr int64_t rx_tile() {
@@ -545,7 +550,11 @@ template <class KT, int VB> struct RxHistShape {
 // value width.
 static int64_t rx_ntiles(int64_t n, int64_t tile) { return (n + tile - 1) / tile; }
 static int64_t rx_min_tile(size_t key_bytes) {
-  if (key_bytes == 8) return rx_tile<uint64_t, 0>();
+  if (key_bytes == 8) {
+    const int64_t a = rx_tile<uint64_t, 0>(), b = rx_tile<uint64_t, 4>(), c = rx_tile<uint64_t, 8>();
+    const int64_t m = a < b ? a : b;
+    return m < c ? m : c;
+  }
   const int64_t a = rx_tile<uint32_t, 0>(), b = rx_tile<uint32_t, 4>(), c = rx_tile<uint32_t, 8>();
   const int64_t m = a < b ? a : b;
   return m < c ? m : c;
