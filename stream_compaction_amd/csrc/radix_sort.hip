@@ -129,27 +129,18 @@ __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
 template <int VB> struct ValBits { using T = uint32_t; };
 template <> struct ValBits<8> { using T = uint64_t; };
 
-// The half-wave ranking (below) takes fewer registers than the full-wave one
-// but twice its LDS instructions, so it pays where the registers it frees let
-// more workgroups share a CU.  Keys only: 2.78 against 3.06 ms for 2^28 u32
-// keys.  32-bit keys with 4-byte values: the values are loaded after the
-// ranking and the positions held packed (below), which brings the 16-wave
-// workgroup to 57 VGPRs and two workgroups per CU: 4.64 against 5.22 ms for
-// 2^28 pairs (with the values held through the ranking instead, one
-// workgroup per CU either way, it lost: 5.36-5.41 against 5.24 ms).  64-bit
-// keys with values: on 8 x 8 tiles it lost (2^27 u64 keys with 4- / 8-byte
-// values 9.14 / 11.79 ms against 8.31 / 10.69), but on 16 x 8 tiles, two
-// workgroups per CU at 46 / 51 VGPRs, it wins: 7.60 / 9.61 ms against 8.28 /
-// 10.66.  It stays off for 32-bit keys with 8-byte values, whose 8 x 16 tiles
-// fit two workgroups per CU by LDS either way.  SCA_RX_HALF_ALL=1 selects it
-// for every width.
-#ifndef SCA_RX_HALF_ALL
-#define SCA_RX_HALF_ALL 0
-#endif
-template <class KT, int VB>
-constexpr bool rx_half_rank() {
-  return SCA_RX_HALF_ALL || VB == 0 || (sizeof(KT) == 4 && VB == 4) || sizeof(KT) == 8;
-}
+// Ranking history, measured on MI355X.  An earlier full-wave form kept the
+// whole wave's 64-bit lane mask in the table entry and the running count in a
+// separate per-wave array: fewer LDS instructions than the half-wave form
+// (below), but more registers.  The half-wave form pays wherever the
+// registers it frees let more workgroups share a CU.  Keys only: 2.78
+// against 3.06 ms for 2^28 u32 keys.  With values, together with the late
+// value loads and packed positions (below) and tiles of 16 waves: 32-bit keys
+// with 4-byte values 4.64 against 5.22 ms (2^28 pairs), with 8-byte values
+// 6.94 against 7.48 ms; 64-bit keys with 4- / 8-byte values 7.60 / 9.61
+// against 8.28 / 10.66 ms (2^27 pairs).  Without those (values held through
+// the ranking, one workgroup per CU, or 8-wave tiles) it had lost: 5.36-5.41
+// against 5.24 ms, and 9.14 / 11.79 against 8.31 / 10.69 ms.
 
 // A buffer resource over [base, base + bytes) for bytes < 2^32: offsets are
 // 32-bit, and accesses past the range read zero or are dropped.
@@ -187,12 +178,11 @@ __device__ __forceinline__ void rx_store(__amdgpu_buffer_rsrc_t r, uint32_t off,
 // Stores: with B32 the outputs are written through buffer resources with
 // 32-bit byte offsets (every array below 4 GiB); else through 64-bit
 // addresses.  FULL tiles skip every per-key range test.
-template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL, class WC,
-          bool HALF = rx_half_rank<KT, VB>()>
+template <class KT, KeyKind KK, int VB, int WAVES, int KPT, bool B32, bool FULL>
 __device__ __forceinline__ void rx_scatter_tile(
     const KT* __restrict__ kin, KT* __restrict__ kout, const void* __restrict__ vin_,
     void* __restrict__ vout_, int64_t n, int shift, int64_t t0, int count,
-    WC (*s_wcnt)[kRxBins + 1], uint32_t* s_start, uint32_t* s_g, uint32_t* s_sum,
+    uint16_t (*s_wcnt)[kRxBins + 1], uint32_t* s_start, uint32_t* s_g, uint32_t* s_sum,
     unsigned char* s_buf) {
   using VT = typename ValBits<VB>::T;
   constexpr int kThreads = 64 * WAVES;
@@ -202,12 +192,11 @@ __device__ __forceinline__ void rx_scatter_tile(
   uint64_t* s_tab = (uint64_t*)s_buf + wave_id() * kBins1;   // this wave's lane-mask table
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
 
-  // With values and the half-wave ranking, the values are loaded only once
+  // With values, the values are loaded only once
   // the keys are ranked, and ranks, reorder positions and output digits are
   // held packed (two or four to a register).  That brings the 16-wave
-  // workgroups of 32-bit keys with 4-byte values to 57-60 VGPRs and of
-  // 64-bit keys with values to 46-51, so two share a CU.
-  constexpr bool kLateV = HALF && VB != 0;
+  // workgroups with values to 41-60 VGPRs, so two share a CU.
+  constexpr bool kLateV = VB != 0;
 
   // ---- load (buffer resources bounded at the tile's keys) ----
   const int wbase = wave * 64 * KPT;                 // the wave's first slot in the tile
@@ -226,7 +215,6 @@ __device__ __forceinline__ void rx_scatter_tile(
 #pragma unroll
     for (int j = 0; j < KPT; ++j) v[j] = rx_load<VT>(vr, vo + (uint32_t)(j * 64 * VB));
   };
-  if constexpr (VB != 0 && !kLateV) load_values();
   auto valid = [&](int j) { return FULL || wbase + j * 64 + lane < count; };
   uint32_t dg[KPT], rank[KPT];
 #pragma unroll
@@ -242,30 +230,11 @@ __device__ __forceinline__ void rx_scatter_tile(
   // bits, read the entry (mask and count), and write back a clear mask with
   // the count advanced; the upper half then does the same and so sees the
   // lower half's keys counted, which keeps ranks in input order.
-  WC* cnt = s_wcnt[wave];
-  if constexpr (!HALF) {
-    // full-wave form: the whole wave's mask in the entry, the running count
-    // in s_wcnt
-    const uint64_t lbit = 1ull << lane;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      uint64_t* e = s_tab + dg[j];
-      __hip_atomic_fetch_or(e, lbit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      const uint64_t match = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      const uint32_t old = __hip_atomic_load(cnt + dg[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_store(e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0u));
-      const uint32_t same = (uint32_t)__builtin_popcountll(match);
-      // every lane of the digit writes the same new count
-      __hip_atomic_store(cnt + dg[j], old + same, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      rank[j] = old + below;
-    }
-  }
+  const uint16_t* cnt = s_wcnt[wave];                // each digit's first slot, after the prefix phase
   const uint32_t hbit = 1u << (lane & 31);
   uint32_t rpk[(KPT + 1) / 2] = {};                  // ranks, two 16-bit halves a register
 #pragma unroll
-  for (int j = 0; j < (HALF ? KPT : 0); ++j) {
+  for (int j = 0; j < KPT; ++j) {
     uint64_t* e = s_tab + dg[j];
     uint32_t r = 0u;
     if (lane < 32) {
@@ -298,9 +267,8 @@ __device__ __forceinline__ void rx_scatter_tile(
     uint32_t h = 0u;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      const uint32_t c = HALF ? (uint32_t)(((const uint64_t*)s_buf)[w * kBins1 + tid] >> 32)
-                              : s_wcnt[w][tid];
-      s_wcnt[w][tid] = (WC)h;
+      const uint32_t c = (uint32_t)(((const uint64_t*)s_buf)[w * kBins1 + tid] >> 32);
+      s_wcnt[w][tid] = (uint16_t)h;
       h += c;
     }
     const uint32_t incl = wave_scan_incl<Op::Add>(h);
@@ -314,7 +282,7 @@ __device__ __forceinline__ void rx_scatter_tile(
     const uint32_t st = s_start[tid] + off;           // the digit's first slot in the tile
     s_g[tid] -= st;                                   // its output position minus that slot
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s_wcnt[w][tid] = (WC)(s_wcnt[w][tid] + st);
+    for (int w = 0; w < WAVES; ++w) s_wcnt[w][tid] = (uint16_t)(s_wcnt[w][tid] + st);
   }
   __syncthreads();
 
@@ -351,21 +319,15 @@ __device__ __forceinline__ void rx_scatter_tile(
   // (positions are below n by construction; the range checks only keep every
   // store inside the output whatever the input)
   const auto okr = rx_rsrc(kout, B32 ? (uint64_t)n * sizeof(KT) : 0);
-  uint32_t dst[KPT];
   uint32_t dpk[(KPT + 3) / 4] = {};                  // kLateV: each slot's digit, four a register
 #pragma unroll
   for (int m = 0; m < KPT; ++m) {
     const int slot = tid + m * kThreads;
-    dst[m] = 0xffffffffu;
     if (FULL || slot < count) {
       const KT key = s_keys[slot];
       const uint32_t d = (uint32_t)((sort_image<KT, KK>(key) >> shift) & 255u);
       const uint32_t g = s_g[d] + (uint32_t)slot;     // modulo 2^32, like the offsets
-      if constexpr (kLateV) {
-        dpk[m >> 2] |= d << ((m & 3) * 8);
-      } else {
-        dst[m] = g;
-      }
+      if constexpr (kLateV) dpk[m >> 2] |= d << ((m & 3) * 8);
       if constexpr (B32) {
         rx_store<KT>(okr, g * (uint32_t)sizeof(KT), key);
       } else {
@@ -386,13 +348,8 @@ __device__ __forceinline__ void rx_scatter_tile(
       for (int i = 0; i < (KPT + 3) / 4; ++i) asm volatile("" : "+v"(dpk[i]));
     }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if constexpr (kLateV) {
-        if (valid(j)) s_vals[(lpk[j >> 1] >> ((j & 1) * 16)) & 0xffffu] = v[j];
-      } else {
-        if (FULL || dg[j] < (uint32_t)kRxBins) s_vals[lpos[j]] = v[j];
-      }
-    }
+    for (int j = 0; j < KPT; ++j)
+      if (valid(j)) s_vals[(lpk[j >> 1] >> ((j & 1) * 16)) & 0xffffu] = v[j];
     __syncthreads();
     VT* vout = (VT*)vout_;
     const auto ovr = rx_rsrc(vout, B32 ? (uint64_t)n * VB : 0);
@@ -401,15 +358,14 @@ __device__ __forceinline__ void rx_scatter_tile(
       const int slot = tid + m * kThreads;
       if (FULL || slot < count) {
         const VT x = s_vals[slot];
-        const uint32_t g = kLateV ? s_g[(dpk[m >> 2] >> ((m & 3) * 8)) & 255u] + (uint32_t)slot
-                                  : dst[m];
+        const uint32_t g = s_g[(dpk[m >> 2] >> ((m & 3) * 8)) & 255u] + (uint32_t)slot;
         if constexpr (B32) {
           rx_store<VT>(ovr, g * (uint32_t)VB, x);
         } else {
           if (g < (uint64_t)n) *gptr<VT>((uintptr_t)(vout + g)) = x;
         }
       }
-      if (kLateV && (m & 3) == 3) asm volatile("" ::: "memory");
+      if ((m & 3) == 3) asm volatile("" ::: "memory");
     }
   }
 }
@@ -422,20 +378,18 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
   constexpr int kBins1 = kRxBins + 1;
-  constexpr bool kHalf = rx_half_rank<KT, VB>();
   constexpr int kSortBytes = kTile * (int)(sizeof(KT) > (size_t)VB ? sizeof(KT) : (size_t)VB);
   constexpr int kTabBytes = WAVES * kBins1 * 8;
   // the digits' first slots sit past the tables until the reorder
   constexpr int kTabStartBytes = kTabBytes + kRxBins * 4;
   constexpr int kBufBytes = kSortBytes > kTabStartBytes ? kSortBytes : kTabStartBytes;
   static_assert(kThreads >= kRxBins, "one thread per digit");
-  // With the half-wave ranking the running counts live in the tables, and
-  // this array only holds each wave's first slot per digit, below the tile
-  // size: 16 bits, which keeps a keys-only workgroup under a quarter of the
-  // CU's LDS (four resident instead of three).
-  using WC = std::conditional_t<kHalf, uint16_t, uint32_t>;
-  static_assert(!kHalf || kTile < 65536, "first slots fit 16 bits");
-  __shared__ WC s_wcnt[WAVES][kBins1];          // per wave: running count, then first slot
+  // The running counts live in the lane-mask tables; this array only holds
+  // each wave's first slot per digit, below the tile size: 16 bits, which
+  // keeps a keys-only workgroup under a quarter of the CU's LDS (four
+  // resident instead of three).
+  static_assert(kTile < 65536, "first slots fit 16 bits");
+  __shared__ uint16_t s_wcnt[WAVES][kBins1];    // per wave: each digit's first slot
   __shared__ uint32_t s_g[kRxBins];             // the digit's first output position (then
                                                 // that minus its first slot in the tile)
   __shared__ uint32_t s_sum[kRxBins / 64];
@@ -449,9 +403,6 @@ __global__ __launch_bounds__(64 * WAVES) void radix_scatter_kernel(
   const int64_t n = live_count(n_cap, n_dev);
   const int count =                                  // keys in this tile
       (int)((n - t0) < kTile ? ((n - t0) > 0 ? (n - t0) : 0) : kTile);
-  if constexpr (!kHalf) {
-    for (int i = tid; i < WAVES * kBins1; i += kThreads) (&s_wcnt[0][0])[i] = 0u;
-  }
   uint64_t* tab = (uint64_t*)s_buf + wave * kBins1;
   for (int i = lane; i < kBins1; i += kWave) tab[i] = 0ull;
   if (tid < kRxBins) s_g[tid] = offsets[(int64_t)tid * ntiles + tile];
@@ -509,20 +460,18 @@ static hipError_t rx_copy(const void* src, void* dst, size_t bytes, hipStream_t 
 }
 
 // Tile shape per key and value width.  32-bit keys alone: 8 waves x 16 keys
-// per thread (8192 keys).  32-bit keys with 4-byte values: 16 waves x 16
-// (16384 keys; with the half-wave ranking, 57 VGPRs and 74,800 bytes of LDS,
-// two workgroups per CU): the longer digit runs halve the
-// write streams per key, which measured 7.40 ms against 8.79 ms for 2^28
-// key-value pairs, while costing the keys-only sort (5.31 ms against 4.19)
-// its occupancy; with the half-wave ranking, 8 x 16 tiles measured 6.32 ms
-// against 4.66.  32-bit keys with 8-byte values: 8 x 16.  64-bit keys alone:
-// 8 waves x 8; with values, 16 x 8 (8192 keys, 74,800 bytes of LDS, two
-// workgroups per CU), for the same longer digit runs.  The LDS reorder buffer
-// holds one tile of the wider of key and value.
+// per thread (8192 keys; 16 x 16 cost the keys-only sort its occupancy, 5.31
+// against 4.19 ms in an earlier version).  With values, 16 waves (two
+// workgroups per CU, 74,800 bytes of LDS each, the reorder buffer holding one
+// tile of the wider of key and value): 16 x 16 (16384 keys) for 32-bit keys
+// with 4-byte values, 16 x 8 (8192) for 8-byte values and for 64-bit keys.
+// Longer digit runs halve the write streams per key: 16 x 16 measured 7.40
+// against 8.79 ms for 2^28 key-value pairs in an earlier version, and 8 x 16
+// measures 6.32 against 4.66 ms now.  64-bit keys alone: 8 waves x 8.
 template <class KT, int VB> struct RxShape { static constexpr int kWaves = 8, kKpt = 8; };
 template <> struct RxShape<uint32_t, 0> { static constexpr int kWaves = 8, kKpt = 16; };
 template <> struct RxShape<uint32_t, 4> { static constexpr int kWaves = 16, kKpt = 16; };
-template <> struct RxShape<uint32_t, 8> { static constexpr int kWaves = 8, kKpt = 16; };
+template <> struct RxShape<uint32_t, 8> { static constexpr int kWaves = 16, kKpt = 8; };
 template <> struct RxShape<uint64_t, 4> { static constexpr int kWaves = 16, kKpt = 8; };
 template <> struct RxShape<uint64_t, 8> { static constexpr int kWaves = 16, kKpt = 8; };
 
