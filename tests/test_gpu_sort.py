@@ -61,6 +61,23 @@ def test_sort_sizes_key_value(dt):
         run_sort(keys, dt, np.arange(n, dtype=np.int32), "i32", label=f"sort {dt} n={n}")
 
 
+EDGE_SIZES = [8191, 8192, 8193, 16383, 16384, 16385, 40_961]
+
+
+@pytest.mark.parametrize("dt,vdt", [("u32", "i64"), ("f32", "f64"), ("u64", "i32"),
+                                    ("i64", "i64"), ("f64", "u64")])
+def test_sort_tile_edges_wide_values(dt, vdt):
+    # 32-bit keys with 8-byte values and 64-bit keys with values run on tiles
+    # of 8,192 keys (16 waves of 8), 32-bit keys with 4-byte values on 16,384:
+    # counts on both sides of one and two tiles, and a ragged multiple
+    for i, n in enumerate(EDGE_SIZES):
+        keys = sort_keys(dt, n, 16_000 + i, "bits")
+        vals = np.arange(n, dtype=np.int64).astype(oracle.STORAGE[vdt]) if vdt in ("i32", "i64") \
+            else np.random.default_rng(16_100 + i).integers(0, 256, size=n * 8, dtype=np.uint8) \
+            .view(oracle.STORAGE[vdt]).copy()
+        run_sort(keys, dt, vals, vdt, label=f"sort {dt} + {vdt} n={n}")
+
+
 @pytest.mark.parametrize("dt,kind", [(d, "dups") for d in KEY_DT] +
                          [("f32", "specials"), ("f64", "specials")])
 def test_sort_duplicates_and_specials_stable(dt, kind):
