@@ -5,19 +5,23 @@
 
 A step is one call of the library on one batch of synthetic input resident in
 HBM; the K timed steps are captured once into a HIP graph and replayed (pass
---eager to issue them one by one).  The headline step is the row-wise exclusive add scan of a bf16
-[8192, 8192] array (N(0,1), seed 1; float32 accumulation, bf16 output rounded
-to nearest even).  Consecutive steps rotate over several input/output buffer
-pairs so that no step finds its data in the 256 MB Infinity Cache left there
-by the previous one.  The other workloads (row scans of fp32 [1024, 4096] and
-bf16 [8192, 8191], the bf16 product scan, the device-wide exclusive and
-inclusive scans, the reductions, reduce-by-key, the radix sort and select) are timed the same way and
-reported inside the same JSON line under "workloads".
+--eager to issue them one by one).  The headline step is the largest
+single-GPU workload: the device-wide exclusive add scan of a flat i32 array of
+2^28 elements, values uniform in {0..15} (seed 2).  Consecutive steps rotate
+over several input/output buffer pairs, so that no step finds its data in the
+256 MB Infinity Cache left there by the previous one.  The other workloads
+(row scans of fp32 [1024, 4096], bf16 [8192, 8192] and [8192, 8191], the bf16
+product scan, the device-wide scans of 2^28 - 37 i32 and of f32/i64 min/max,
+the inclusive scan, the reductions, reduce-by-key, the radix sort and select)
+are timed the same way and reported inside the same JSON line under
+"workloads".
 
 Prints ONE JSON line.  "value" is elements/s of the headline workload (wall
-clock over the K timed steps); "roofline" rates the headline kernel by its
-algorithmic bytes (read n + write n) over its average launch duration from HIP
-events; "cpu_baseline" times the CPU oracle on the same workload on the host.
+clock over the K timed steps); "roofline" rates the headline call by its
+algorithmic bytes (read n + write n) over its average duration from HIP
+events on the launch stream (the call is the scan kernel plus the small kernel
+that resets its tile descriptors); "cpu_baseline" times the CPU oracle on the
+same workload on one host core.
 """
 import argparse
 import hashlib
@@ -34,6 +38,7 @@ if ROOT not in sys.path:
 PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
 METRIC = "scan elements/s and achieved HBM GB/s (% of peak), 1 MI355X"
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+HEAD_BYTES = (1 << 28) * 4 * 2   # the headline's read + write bytes (also what copy16 moves)
 KERNEL_SOURCES = {           # sources whose change invalidates stored counter readings
     "scan_rows": ["device.hpp", "scan_rows.hip"],
     "scan_device": ["device.hpp", "scan_device.hip"],
@@ -112,7 +117,7 @@ def pmc_summary(fetch_csv, write_csv, command, select_key="select_p0.5"):
     if os.path.exists(PMC_FILE):
         with open(PMC_FILE) as fh:
             out.update(json.load(fh))
-    out["copy16"] = {"bytes": 268435456, "fetch_kib": fetch["copy16"],
+    out["copy16"] = {"bytes": HEAD_BYTES, "fetch_kib": fetch["copy16"],
                      "write_kib": write["copy16"], "command": command}
     for prefix, (key, kind) in KERNEL_KEYS.items():
         key = select_key if key == "select_p0.5" else key
@@ -288,22 +293,35 @@ def main():
         results[name] = r
         return r
 
-    # ---------------- headline: bf16 [8192, 8192] exclusive row scan ----------------
+    # ---------------- headline: i32 device-wide exclusive add scan, n = 2^28 ----------------
     head = None
-    rows, n = wl.FULL["rows_bf16"]
-    head_bytes = rows * n * 2 * 2
-    if want("rows_bf16_excl"):
-        xb = wl.rows_bf16(rows, n)
-        xs = [bf16_dev(xb) for _ in range(args.sets)]
+    n_head = wl.FULL["dev_i32"]
+    head_bytes = n_head * 4 * 2
+    assert head_bytes == HEAD_BYTES
+    x_head = wl.dev_i32()
+    if want("dev_i32_add"):
+        xs = [torch.from_numpy(x_head).to(dev) for _ in range(args.sets)]
         ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
-        wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "add", True, ys[i % args.sets]),
-                          args.steps, args.warmup)
-        head = record("rows_bf16_excl", rows * n, head_bytes, wall, per, args.steps)
+        s_head = torch.empty(sc.scan_device_scratch_bytes(n_head, "i32"), dtype=torch.uint8,
+                             device=dev)
+        wall, per = timed(lambda i: sc.scan_device(xs[i % args.sets], "add", ys[i % args.sets],
+                                                   s_head), args.steps, args.warmup)
+        head = record("dev_i32_add", n_head, head_bytes, wall, per, args.steps,
+                      "includes the descriptor-reset fill kernel")
         head["wall_s"] = wall
         del xs, ys
 
     # ---------------- the other workloads ----------------
     K, W = args.sub_steps, 3
+    rows, n = wl.FULL["rows_bf16"]
+    if want("rows_bf16_excl"):
+        xb = wl.rows_bf16(rows, n)
+        xs = [bf16_dev(xb) for _ in range(args.sets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
+        wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "add", True, ys[i % args.sets]),
+                          K, W)
+        record("rows_bf16_excl", rows * n, rows * n * 4, wall, per, K)
+        del xs, ys
     if want("rows_bf16_ragged_excl"):
         r2, n2 = wl.FULL["rows_bf16_ragged"]
         xb2 = wl.rows_bf16(r2, n2)
@@ -325,10 +343,10 @@ def main():
         wall, per = timed(lambda i: sc.scan_rows(xs[i % sets], "add", excl, ys[i % sets]), K, W)
         record(name, r1 * n1, r1 * n1 * 8, wall, per, K)
         del xs, ys
-    for name, n3 in (("dev_i32_add", wl.FULL["dev_i32"]), ("dev_i32_add_odd", wl.FULL["dev_i32_odd"])):
+    for name, n3 in (("dev_i32_add_odd", wl.FULL["dev_i32_odd"]),):
         if not want(name):
             continue
-        x3 = torch.from_numpy(wl.dev_i32()[:n3]).to(dev)
+        x3 = torch.from_numpy(x_head[:n3]).to(dev)
         y3 = torch.empty_like(x3)
         s3 = torch.empty(sc.scan_device_scratch_bytes(n3, "i32"), dtype=torch.uint8, device=dev)
         wall, per = timed(lambda i: sc.scan_device(x3, "add", y3, s3), K, W)
@@ -354,12 +372,12 @@ def main():
         ys = [torch.empty_like(xs[0]) for _ in range(args.sets)]
         wall, per = timed(lambda i: sc.scan_rows(xs[i % args.sets], "mul", True, ys[i % args.sets]),
                           K, W)
-        record("rows_bf16_prod_excl", rows * n, head_bytes, wall, per, K,
+        record("rows_bf16_prod_excl", rows * n, rows * n * 4, wall, per, K,
                "product scan, factors +-(1 + U[-1/64, 1/64)) in bf16, seed 12")
         del xs, ys
     if want("dev_i32_add_incl"):
         n3 = wl.FULL["dev_i32"]
-        x3 = torch.from_numpy(wl.dev_i32()).to(dev)
+        x3 = torch.from_numpy(x_head).to(dev)
         y3 = torch.empty_like(x3)
         s3 = torch.empty(sc.scan_device_scratch_bytes(n3, "i32"), dtype=torch.uint8, device=dev)
         wall, per = timed(lambda i: sc.scan_device_inclusive(x3, "add", y3, s3), K, W)
@@ -477,37 +495,30 @@ def main():
                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
             assert rc == 0, rc
         wall, per = timed(cp, args.steps, args.warmup)
-        copy = record("copy16", half // 2, head_bytes, wall, per, args.steps,
+        copy = record("copy16", half // 4, head_bytes, wall, per, args.steps,
                       "16-byte copy kernel moving the headline's read+write bytes")
         del srcs, dsts
 
     # ---------------- CPU oracle baseline on the headline workload ----------------
+    # The oracle is a sequential left fold, so it runs on one core; the whole
+    # 2^28-element workload takes well under a second per run.
     cpu = None
     if not args.no_cpu and head is not None:
-        from concurrent.futures import ThreadPoolExecutor
-
         import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
-        blocks = np.array_split(np.arange(rows), threads)
-
-        def run_block(b):
-            oracle.scan(xb[b[0]:b[-1] + 1], "bf16", "add", exclusive=True)
-
         times = []
-        with ThreadPoolExecutor(threads) as ex:
-            for _ in range(3):
-                t0 = time.perf_counter()
-                list(ex.map(run_block, blocks))
-                times.append(time.perf_counter() - t0)
+        for _ in range(5):
+            t0 = time.perf_counter()
+            oracle.scan(x_head, "i32", "add", exclusive=True)
+            times.append(time.perf_counter() - t0)
         t = float(np.median(times))
-        cpu = {"value": rows * n / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
-               "sample": f"the full workload, bf16 [{rows}, {n}] exclusive add, rows split "
-                         f"over {threads} threads, median of 3 runs ({t:.3f} s each)",
+        cpu = {"value": n_head / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full workload: exclusive add scan of the same 2^28 i32 values "
+                         f"(seed 2) on one core, median of 5 runs ({t:.3f} s each)",
                "cpu": cpu_model()}
 
     # ---------------- stored counter readings -> HBM traffic per launch ----------------
-    traffic = traffic_bytes("rows_bf16_excl", "scan_rows")
-    for key, kind in (("dev_i32_add", "scan_device"), ("select_p0.5", "select"),
+    traffic = traffic_bytes("dev_i32_add", "scan_device")
+    for key, kind in (("rows_bf16_excl", "scan_rows"), ("select_p0.5", "select"),
                       ("select_p0.01", "select"),
                       ("reduce_i32_add", "reduce"), ("reduce_by_key", "reduce_by_key")):
         t = traffic_bytes(key, kind)
@@ -524,7 +535,7 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": METRIC,
-        "value": (rows * n * args.steps / head["wall_s"]) if head else None,
+        "value": (n_head * args.steps / head["wall_s"]) if head else None,
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -533,19 +544,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i32",
         "data": "synthetic",
-        "config": {"workload": "row-wise exclusive add scan along the last axis, bf16 "
-                               "[8192, 8192] N(0,1) seed 1, float32 accumulation, bf16 output "
-                               "rounded nearest-even",
-                   "rows": rows, "n": n, "io_dtype": "bf16", "accumulate": "f32",
+        "config": {"workload": "device-wide exclusive add scan of a flat i32 array, n = 2^28, "
+                               "values uniform integers in [0, 15] (seed 2)",
+                   "n": n_head, "io_dtype": "i32", "op": "add", "exclusive": True,
                    "buffer_sets": args.sets},
     }
     if head:
         achieved = head_bytes / (head["kernel_ms_avg"] * 1e-3) / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                            "traffic": traffic, "kernel": "scan_rows_kernel<bf16, add, excl>",
+                            "traffic": traffic,
+                            "kernel": "scan_device_kernel<i32, add, exclusive> with its "
+                                      "descriptor-reset fill kernel (the whole call)",
                             "bytes_per_launch": head_bytes}
         if copy:
             line["roofline"]["copy16_GBps"] = round(copy["GBps"], 1)

@@ -43,7 +43,9 @@
  *    metaltile-std src/mlx/scan.rs.  Integer add wraps modulo 2^w.  min/max
  *    and integer results are deterministic and exact; floating add may be
  *    regrouped, so its last bits can differ from a sequential fold ("Algorithms"
- *    page, "Common conventions", floating-point non-associativity).
+ *    page, "Common conventions", floating-point non-associativity), and for the
+ *    device-wide scans and reduce-by-key also from one run to the next (the
+ *    look-back combines whichever predecessor descriptors are ready).
  */
 #ifndef STREAM_COMPACTION_AMD_SCAN_H
 #define STREAM_COMPACTION_AMD_SCAN_H

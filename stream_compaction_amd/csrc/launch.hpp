@@ -41,7 +41,7 @@ hipError_t launch_reduce_by_key(const void* keys, const void* values, void* keys
                                 Fmt vfmt, void* scratch, hipStream_t stream,
                                 const int32_t* n_dev = nullptr);
 
-// Radix sort (n < 2^30); value_bytes 0 (keys only), 4 or 8.
+// Radix sort (0 <= n <= INT32_MAX); value_bytes 0 (keys only), 4 or 8.
 size_t radix_sort_scratch(int64_t n, size_t key_bytes);
 hipError_t launch_radix_sort(void* keys, void* tmp_keys, void* values, void* tmp_values, int64_t n,
                              Fmt kfmt, int value_bytes, int end_bit, void* scratch,

@@ -2,8 +2,10 @@
 // ("Algorithms" page, Quadrants user guide, section qd.algorithms.sort:
 // ascending, stable, 8-bit digits, keys mapped to a sortable unsigned image;
 // each digit pass is a tile histogram, a scan of the digit-major histogram
-// buffer, and a scatter).  Per pass, on tiles of 8192 (32-bit keys) or 4096
-// (64-bit keys) keys:
+// buffer, and a scatter).  Per pass, on tiles whose size depends on the key
+// and value widths (RxShape below: 8,192 keys for 32-bit keys alone or with
+// 8-byte values, 16,384 for 32-bit keys with 4-byte values, 4,096 for 64-bit
+// keys alone and 8,192 for 64-bit keys with values):
 //   1. radix_tile_hist_kernel: every tile counts its keys per digit (per-wave
 //      LDS counters) and writes the 256 counts digit-major,
 //      hist[d * ntiles + t];

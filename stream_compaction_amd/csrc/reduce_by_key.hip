@@ -302,7 +302,10 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     if (tile > 0) {
       // fallback for a late predecessor: fold its input in element order, a
       // few loads at a time (this rare path must not raise the kernel's
-      // register count, which sets how many workgroups fit on a CU)
+      // register count, which sets how many workgroups fit on a CU).  Counts
+      // and integer sums are exactly what that tile would publish; float32
+      // sums are grouped differently from its data waves' tail sums, so they
+      // may differ in the last bits (within the float-add tolerance)
       auto reduce_tile = [&](int64_t t) -> W {
         constexpr int kG = 2;
         static_assert(kTileVecs % (kG * kWave) == 0, "whole groups of loads");

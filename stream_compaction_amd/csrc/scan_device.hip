@@ -144,31 +144,40 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
     };
     W prefix = id;
     if (tile > 0) {
-      // fallback for a late predecessor: reduce its input in element order,
-      // a few loads at a time (this rare path must not raise the kernel's
-      // register count, which sets how many workgroups fit on a CU)
+      // fallback for a late predecessor: reduce its input with the grouping
+      // its own data waves use (each wave's K loads folded from the identity,
+      // then the wave totals in wave order), so the result is bit for bit the
+      // aggregate that tile would publish, floating add included; a few loads
+      // at a time (this rare path must not raise the kernel's register count,
+      // which sets how many workgroups fit on a CU)
       auto reduce_tile = [&](int64_t t) -> W {
         constexpr int kG = 4;
-        static_assert(kTileVecs % (kG * kWave) == 0, "whole groups of loads");
+        static_assert(K % kG == 0, "a wave's run is whole groups of loads");
         const int64_t first = t * kTileVecs;
         const int64_t left = v_last + 1 - first;
         const int64_t nv = left <= 0 ? 0 : (left < kTileVecs ? left : kTileVecs);
         const Buf buf(in_base + first * VB, nv * VB);
         W acc = id;
 #pragma unroll 1
-        for (int g = 0; g < (int)(kTileVecs / (kG * kWave)); ++g) {
-          typename IO::Raw r[kG];
+        for (int w = 0; w < WD; ++w) {
+          W wsum = id;
+#pragma unroll 1
+          for (int g = 0; g < K / kG; ++g) {
+            const int j0 = w * K + g * kG;      // the tile's load index
+            typename IO::Raw r[kG];
 #pragma unroll
-          for (int j = 0; j < kG; ++j)
-            r[j] = IO::load(buf, (uint32_t)(((g * kG + j) * kWave + lane) * VB));
+            for (int j = 0; j < kG; ++j)
+              r[j] = IO::load(buf, (uint32_t)(((j0 + j) * kWave + lane) * VB));
 #pragma unroll
-          for (int j = 0; j < kG; ++j) {
-            W y[E];
-            unpack(first + (g * kG + j) * kWave, r[j], y);
+            for (int j = 0; j < kG; ++j) {
+              W y[E];
+              unpack(first + (j0 + j) * kWave, r[j], y);
 #pragma unroll
-            for (int k = 1; k < E; ++k) y[k] = combine<O>(y[k - 1], y[k]);
-            acc = combine<O>(acc, readlane(wave_scan_incl<O>(y[E - 1]), kWave - 1));
+              for (int k = 1; k < E; ++k) y[k] = combine<O>(y[k - 1], y[k]);
+              wsum = combine<O>(wsum, readlane(wave_scan_incl<O>(y[E - 1]), kWave - 1));
+            }
           }
+          acc = w == 0 ? wsum : combine<O>(acc, wsum);
         }
         return acc;
       };

@@ -28,7 +28,7 @@ namespace sca {
 
 template <class F, Op O, bool EXCL, int E, int WPR, int K>
 __global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, uintptr_t out_base,
-                                                            int64_t rows, int64_t n, int64_t ph) {
+                                                            int64_t row0, int64_t n, int64_t ph) {
   using S = typename F::S;
   using W = typename F::W;
   using IO = VecIO<S, E>;
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, 
   __shared__ W s_tot[2][WPR];
 
   const int lane = lane_id(), wave = wave_id();
-  const int64_t row = blockIdx.x;
+  const int64_t row = row0 + blockIdx.x;
   // valid window elements of this row, and the vectors that cover them
   const int64_t lo = row * n + ph, hi = lo + n;
   const int64_t v_first = lo / E, v_last = (hi - 1) / E;
@@ -125,11 +125,21 @@ __global__ __launch_bounds__(64 * WPR) void scan_rows_kernel(uintptr_t in_base, 
   }
 }
 
+// A dispatch counts its work-items in 32 bits per grid dimension, so one
+// launch takes fewer than 2^32 / 512 rows (512 threads being the largest
+// workgroup here); more rows go out as several launches, each told its first
+// row (rows are independent, so the launches need no ordering between them).
+constexpr int64_t kRowsPerLaunch = 1ll << 22;
+
 template <class F, Op O, bool EXCL, int E, int WPR, int K>
 static void launch_rows_cfg(uintptr_t in_base, uintptr_t out_base, int64_t rows, int64_t n,
                             int64_t ph, hipStream_t stream) {
-  scan_rows_kernel<F, O, EXCL, E, WPR, K><<<dim3((unsigned)rows), dim3(64 * WPR), 0, stream>>>(
-      in_base, out_base, rows, n, ph);
+  static_assert(64 * WPR * kRowsPerLaunch < (1ll << 32), "a launch's work-items fit 32 bits");
+  for (int64_t row0 = 0; row0 < rows; row0 += kRowsPerLaunch) {
+    const int64_t nr = rows - row0 < kRowsPerLaunch ? rows - row0 : kRowsPerLaunch;
+    scan_rows_kernel<F, O, EXCL, E, WPR, K><<<dim3((unsigned)nr), dim3(64 * WPR), 0, stream>>>(
+        in_base, out_base, row0, n, ph);
+  }
 }
 
 // Launch shape by the number of 16-byte vectors a row touches, measured on

@@ -18,6 +18,8 @@
   float32 product.
 """
 import numpy as np
+
+import oracle
 import torch
 
 FP_REL, FP_ABS = 1e-5, 1e-6
@@ -109,3 +111,31 @@ def check_fp_mul(gpu, ref, m, dtype, label=""):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(bound > 0, err / bound, 0.0)
     return float(r.max()) if r.size else 0.0
+
+
+def check_stable_by_image(keys_in, keys_out, idx_out, dt, label):
+    """The stable ascending order by the oracle's sort image is unique, and an
+    output (keys, original index of each key) is that order exactly when:
+      - the carried indices are a permutation of [0, n);
+      - every output key is the input key at its carried index, bit for bit;
+      - the oracle's images of the output keys never decrease, and where two
+        neighbours' images are equal their indices increase (stability).
+    Checked with numpy, so no library sort is involved: the oracle's order
+    definition (oracle.sort_image) applied at sizes where the oracle's own
+    argsort would take minutes."""
+    n = keys_in.size
+    assert keys_out.size == n and idx_out.size == n, f"{label}: length changed"
+    if n == 0:
+        return
+    assert idx_out.min() >= 0 and idx_out.max() < n, f"{label}: index out of range"
+    seen = np.zeros(n, dtype=bool)
+    seen[idx_out] = True
+    assert seen.all(), f"{label}: not a permutation"
+    del seen
+    assert np.array_equal(keys_out.view(np.uint8), keys_in[idx_out].view(np.uint8)), \
+        f"{label}: a key moved without its index"
+    img = oracle.sort_image(keys_out, dt)
+    step_up = img[1:] > img[:-1]
+    tie_ok = (img[1:] == img[:-1]) & (idx_out[1:] > idx_out[:-1])
+    bad = ~(step_up | tie_ok)
+    assert not bad.any(), f"{label}: out of order at {int(np.argmax(bad))}"

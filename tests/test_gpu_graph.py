@@ -1,9 +1,14 @@
 """The library's calls captured into a HIP graph: every replay, with the
 program's own eager work and synchronizations in between, must reproduce the
-eager result bit for bit.  Every kernel is deterministic (row scans, device
-scans and reductions have a fixed combine order for a given size and pointer
-alignment; select is exact), and each call resets its descriptors with a fill
-kernel rather than hipMemsetAsync, so it can sit in a graph."""
+eager result bit for bit.  Every call below is deterministic: row scans and
+reductions combine in a fixed order for a given size and pointer alignment,
+and the device scans here are integer or min/max scans and select, whose
+results are exact whatever order the look-back combines descriptors in.  (A
+floating-add device scan is not in this list: its look-back may take a
+predecessor's inclusive prefix or its aggregate, depending on timing, so its
+last bits can differ from run to run, within the float tolerance.)  Each call
+resets its descriptors with a fill kernel rather than hipMemsetAsync, so it
+can sit in a graph."""
 import numpy as np
 import pytest
 import torch

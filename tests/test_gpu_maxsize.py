@@ -142,3 +142,47 @@ def test_radix_sort_max_count_key_value():
         assert torch.equal(keys[a:b].to(torch.int64), j), f"keys [{a}, {b})"
         assert torch.equal(vals[a:b].to(torch.int64), j.mul_(a_inv).remainder_(N)), \
             f"values [{a}, {b})"
+
+
+@pytest.mark.parametrize("rows", [(1 << 26) + 1, N], ids=["2^26+1", "2^31-1"])
+def test_scan_rows_many_one_element_rows(rows):
+    # more rows than one dispatch can hold (its work-items are counted in 32
+    # bits), so the rows go out in several launches.  With one element per row,
+    # each row's inclusive prefix is its element and its exclusive prefix the
+    # identity: here x[r] = (r mod 7) - 3 in bf16 (exact), identity 0 for add
+    # and -inf for max.
+    note(f"scan_rows bf16 [{rows}, 1] add/max")
+    x = mod7_input(rows).to(torch.bfloat16).view(rows, 1)
+    for op, excl in (("add", False), ("add", True), ("max", True)):
+        out = sc.scan_rows(x, op=op, exclusive=excl)
+        torch.cuda.synchronize()
+        for a, b in chunks(rows):
+            if not excl:
+                want = x[a:b]
+            else:
+                want = torch.full((b - a, 1), 0.0 if op == "add" else float("-inf"),
+                                  dtype=torch.bfloat16, device="cuda")
+            assert torch.equal(out[a:b], want), f"{op} excl={excl} rows [{a}, {b})"
+        del out
+
+
+def test_scan_rows_many_three_element_rows():
+    # rows [1, -1, r mod 5] (f32): exclusive [0, 1, 0], inclusive [1, 0, r mod 5],
+    # over 2^26 + 1 rows (several launches; rows straddle 16-byte vectors)
+    rows = (1 << 26) + 1
+    note(f"scan_rows f32 [{rows}, 3] add")
+    x = torch.empty((rows, 3), dtype=torch.float32, device="cuda")
+    x[:, 0] = 1.0
+    x[:, 1] = -1.0
+    x[:, 2] = torch.arange(rows, dtype=torch.int32, device="cuda").remainder_(5).float()
+    for excl in (False, True):
+        out = sc.scan_rows(x, op="add", exclusive=excl)
+        torch.cuda.synchronize()
+        for a, b in chunks(rows):
+            if excl:
+                want = torch.tensor([0.0, 1.0, 0.0], device="cuda").expand(b - a, 3)
+            else:
+                want = torch.stack([torch.ones(b - a, device="cuda"),
+                                    torch.zeros(b - a, device="cuda"), x[a:b, 2]], dim=1)
+            assert torch.equal(out[a:b], want), f"excl={excl} rows [{a}, {b})"
+        del out

@@ -9,7 +9,7 @@ import oracle
 import stream_compaction_amd as sc
 import workloads
 from gpu_util import from_dev, note, to_dev
-from parity import check_exact
+from parity import check_exact, check_stable_by_image
 
 pytestmark = pytest.mark.gpu
 
@@ -61,19 +61,22 @@ def test_sort_sizes_key_value(dt):
         run_sort(keys, dt, np.arange(n, dtype=np.int32), "i32", label=f"sort {dt} n={n}")
 
 
-EDGE_SIZES = [8191, 8192, 8193, 16383, 16384, 16385, 40_961]
+EDGE_SIZES = [8191, 8192, 8193, 16383, 16384, 16385, 32769, 40_961]
 
 
 @pytest.mark.parametrize("dt,vdt", [("u32", "i64"), ("f32", "f64"), ("u64", "i32"),
-                                    ("i64", "i64"), ("f64", "u64")])
+                                    ("i64", "i64"), ("f64", "u64"), ("u32", "i32"),
+                                    ("i32", "f32"), ("f32", "u32")])
 def test_sort_tile_edges_wide_values(dt, vdt):
     # 32-bit keys with 8-byte values and 64-bit keys with values run on tiles
-    # of 8,192 keys (16 waves of 8), 32-bit keys with 4-byte values on 16,384:
-    # counts on both sides of one and two tiles, and a ragged multiple
+    # of 8,192 keys (16 waves of 8), 32-bit keys with 4-byte values on 16,384
+    # (16 waves of 16): counts on both sides of one and two tiles of either
+    # size, and ragged multiples
     for i, n in enumerate(EDGE_SIZES):
         keys = sort_keys(dt, n, 16_000 + i, "bits")
         vals = np.arange(n, dtype=np.int64).astype(oracle.STORAGE[vdt]) if vdt in ("i32", "i64") \
-            else np.random.default_rng(16_100 + i).integers(0, 256, size=n * 8, dtype=np.uint8) \
+            else np.random.default_rng(16_100 + i).integers(
+                0, 256, size=n * np.dtype(oracle.STORAGE[vdt]).itemsize, dtype=np.uint8) \
             .view(oracle.STORAGE[vdt]).copy()
         run_sort(keys, dt, vals, vdt, label=f"sort {dt} + {vdt} n={n}")
 
@@ -150,33 +153,56 @@ def test_lookback_recovery_build_sort():
     check_exact(vd.cpu().numpy(), ov, "fallback build values")
 
 
-def test_sort_arrays_past_4gib():
-    """Arrays of 4 GiB and more take the scatter's 64-bit-address stores (below
-    that, 32-bit buffer offsets).  At these sizes the check is against the
-    library sort torch ships (stable, in unsigned key order): keys, and the
-    original index carried as an 8-byte value, must match it exactly."""
+def test_sort_keys_only_past_4gib():
+    """u64 keys only, n = 2^29 + 7 (4 GiB): the scatter's 64-bit-address stores
+    (below 4 GiB it uses 32-bit buffer offsets).  Keys come from 997 distinct
+    bit patterns; the output must be the input's multiset in the oracle's image
+    order (non-decreasing images; equal keys are indistinguishable, so this is
+    the stable order)."""
     g = torch.Generator(device="cuda").manual_seed(20_000)
-    top = torch.tensor(-(1 << 63), dtype=torch.int64, device="cuda")
-    # u64 keys only, from 997 distinct bit patterns
     n = (1 << 29) + 7
     note(f"sort u64 keys only n={n}")
     alphabet = torch.randint(-(1 << 63), (1 << 63) - 1, (997,), generator=g, device="cuda",
                              dtype=torch.int64)
-    keys = alphabet[torch.randint(0, 997, (n,), generator=g, device="cuda")]
-    ref = torch.sort(keys ^ top, stable=True).values ^ top
+    sym = torch.randint(0, 997, (n,), generator=g, device="cuda")
+    keys = alphabet[sym]
+    counts_in = torch.bincount(sym, minlength=997).cpu().numpy()
+    del sym
     sc.radix_sort(keys, key_dtype="u64")
     torch.cuda.synchronize()
-    assert torch.equal(keys, ref), "u64 keys past 4 GiB"
-    del keys, ref
-    # u32 keys with i64 values (each key's index), from 1,009 distinct keys
+    out = keys.cpu().numpy().view(np.uint64)
+    del keys
+    note("  checking on the host")
+    al = alphabet.cpu().numpy().view(np.uint64)
+    img = oracle.sort_image(out, "u64")
+    assert not (img[1:] < img[:-1]).any(), "u64 keys past 4 GiB: out of order"
+    del img
+    order = np.argsort(al)
+    pos = np.searchsorted(al[order], out)
+    assert np.array_equal(al[order][pos], out), "u64 keys past 4 GiB: a key not in the input"
+    assert np.array_equal(np.bincount(order[pos], minlength=997), counts_in), \
+        "u64 keys past 4 GiB: multiset changed"
+
+
+@pytest.mark.parametrize("kdt", ["u32", "u64"])
+def test_sort_key_value_past_4gib(kdt):
+    """u32 or u64 keys with i64 values (each key's original index), n = 2^29 + 3:
+    the values array passes 4 GiB, so the scatter takes its 64-bit-address
+    stores.  Keys come from 1,009 distinct bit patterns (long runs of equal
+    keys, so stability matters); checked against the oracle's order."""
+    g = torch.Generator(device="cuda").manual_seed(20_001 if kdt == "u32" else 20_002)
     n = (1 << 29) + 3
-    note(f"sort u32 keys + i64 values n={n}")
-    alpha32 = torch.randint(-(1 << 31), (1 << 31) - 1, (1009,), generator=g, device="cuda",
-                            dtype=torch.int32)
-    keys = alpha32[torch.randint(0, 1009, (n,), generator=g, device="cuda")]
+    note(f"sort {kdt} keys + i64 values n={n}")
+    tdt = torch.int32 if kdt == "u32" else torch.int64
+    lo, hi = (-(1 << 31), (1 << 31) - 1) if kdt == "u32" else (-(1 << 63), (1 << 63) - 1)
+    alpha = torch.randint(lo, hi, (1009,), generator=g, device="cuda", dtype=tdt)
+    keys = alpha[torch.randint(0, 1009, (n,), generator=g, device="cuda")]
+    keys_in = keys.cpu().numpy().view(np.uint32 if kdt == "u32" else np.uint64)
     vals = torch.arange(n, dtype=torch.int64, device="cuda")
-    ref = torch.sort(keys.to(torch.int64) & 0xFFFFFFFF, stable=True)
-    sc.radix_sort(keys, vals, key_dtype="u32", value_dtype="i64")
+    sc.radix_sort(keys, vals, key_dtype=kdt, value_dtype="i64")
     torch.cuda.synchronize()
-    assert torch.equal(keys.to(torch.int64) & 0xFFFFFFFF, ref.values), "u32 keys past 4 GiB"
-    assert torch.equal(vals, ref.indices), "i64 values past 4 GiB (stability)"
+    keys_out = keys.cpu().numpy().view(keys_in.dtype)
+    idx = vals.cpu().numpy()
+    del keys, vals
+    note("  checking on the host")
+    check_stable_by_image(keys_in, keys_out, idx, kdt, f"{kdt} keys + i64 values past 4 GiB")

@@ -6,7 +6,7 @@ import numpy as np
 
 import oracle
 import workloads
-from parity import check_fp_add, check_fp_mul
+from parity import check_fp_add, check_fp_mul, check_stable_by_image
 
 
 def _raises(fn):
@@ -71,3 +71,33 @@ def test_fp_mul_rule_accepts_float32_products_and_rejects_a_dropped_factor():
     badb = exc.copy()
     badb[:, 3000:] /= xf[:, 3000:3001]
     assert _raises(lambda: check_fp_mul(workloads.to_bf16_bits(badb), refb, mb, "bf16", "dropped"))
+
+
+def test_stable_order_rule_accepts_the_oracle_sort_and_rejects_mistakes():
+    rng = np.random.default_rng(31)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1.0, -1.0, 2.5], np.float32)
+    cases = [(rng.integers(0, 5, size=3000).astype(np.uint32), "u32"),
+             (rng.integers(-(1 << 63), (1 << 63) - 1, size=3000, dtype=np.int64), "i64"),
+             (specials[rng.integers(0, specials.size, size=3000)], "f32")]
+    for keys, dt in cases:
+        ok, ov = oracle.sort(keys, dt, np.arange(keys.size, dtype=np.int64))
+        check_stable_by_image(keys, ok, ov, dt, f"oracle sort {dt}")
+        # two equal-image neighbours in the wrong order (stability broken)
+        img = oracle.sort_image(ok, dt)
+        ties = np.flatnonzero(img[1:] == img[:-1])
+        if ties.size:
+            i = int(ties[0])
+            bk, bv = ok.copy(), ov.copy()
+            bk[[i, i + 1]], bv[[i, i + 1]] = bk[[i + 1, i]], bv[[i + 1, i]]
+            assert _raises(lambda: check_stable_by_image(keys, bk, bv, dt, "tie swapped"))
+        # a key that does not travel with its index
+        bk = ok.copy()
+        bk[[0, -1]] = bk[[-1, 0]]
+        assert _raises(lambda: check_stable_by_image(keys, bk, ov, dt, "key moved alone"))
+        # an index repeated (not a permutation)
+        bv = ov.copy()
+        bv[1] = bv[0]
+        assert _raises(lambda: check_stable_by_image(keys, ok, bv, dt, "index repeated"))
+        # keys in descending image order, carried consistently
+        assert _raises(lambda: check_stable_by_image(keys, ok[::-1].copy(), ov[::-1].copy(), dt,
+                                                     "reversed"))
