@@ -277,6 +277,29 @@ const char* scan_status_str(scan_status s);
 /* hipError_t value behind the calling thread's last SCAN_EHIP (0 if none). */
 int scan_last_hip_error(void);
 
+/*
+ * scan_device without a scratch argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operation, arguments, results and
+ * kernels as scan_device (exclusive scan, out[0] = identity).  It allocates
+ * nothing: the tile descriptors live in a static device array of
+ * SCAN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends; the array of the calling thread's current
+ * device is used, so `stream` must belong to that device.  Each call clears
+ * the descriptors it uses (a fill kernel on `stream`), so nothing carries
+ * over from one call to the next, but every such call on one GPU shares the
+ * array: two calls in flight at the same time on one GPU (other streams,
+ * other threads) race and give wrong results.
+ *
+ *   n          0 <= n and scan_device_scratch_bytes(n, dtype) <=
+ *              SCAN_NOALLOC_SCRATCH_BYTES (n <= 469,754,880; a larger n
+ *              returns SCAN_ESCRATCH before anything is launched).
+ *   others     as for scan_device.
+ */
+#define SCAN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+scan_status scan_device_noalloc(const void* in, void* out, int64_t n, scan_dtype dtype,
+                                scan_op op, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,7 +47,8 @@ EXPORTS = ("scan_rows", "scan_device", "scan_device_inclusive", "scan_device_scr
            "reduce_by_key_scratch_bytes", "radix_sort", "radix_sort_scratch_bytes",
            "select_compact", "select_compact_scratch_bytes", "scan_device_devn",
            "scan_device_inclusive_devn", "reduce_device_devn", "reduce_by_key_devn",
-           "radix_sort_devn", "select_compact_devn", "scan_status_str", "scan_last_hip_error")
+           "radix_sort_devn", "select_compact_devn", "scan_device_noalloc", "scan_status_str",
+           "scan_last_hip_error")
 
 _lib = None
 
@@ -77,6 +78,8 @@ def load(path):
     L.scan_device_scratch_bytes.restype = sz
     L.scan_device.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
     L.scan_device.restype = i32
+    L.scan_device_noalloc.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.scan_device_noalloc.restype = i32
     L.scan_device_inclusive.argtypes = [vp, vp, i64, i32, i32, vp, sz, vp]
     L.scan_device_inclusive.restype = i32
     L.reduce_device_scratch_bytes.argtypes = [i64, i32]
@@ -204,6 +207,22 @@ def scan_device(x, op="add", out=None, scratch=None, stream=None, dtype=None, n_
     L = lib()
     fn = L.scan_device if n_live is None else L.scan_device_devn
     return _scan_device(fn, x, op, out, scratch, stream, dtype, n_live)
+
+
+def scan_device_noalloc(x, op="add", out=None, stream=None, dtype=None):
+    """scan_device with the library's static per-GPU scratch (the C entry point
+    allocates nothing; calls overlapping on one GPU race)."""
+    torch = _torch()
+    if x.dim() != 1:
+        raise ValueError("x must be 1-D")
+    name = _name(x, dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    check(lib().scan_device_noalloc(_dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0],
+                                    DTYPE_CODES[name], OP_CODES[op], _stream(stream)))
+    return out
 
 
 def scan_device_inclusive(x, op="add", out=None, scratch=None, stream=None, dtype=None,

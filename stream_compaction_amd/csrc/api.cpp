@@ -151,6 +151,32 @@ scan_status scan_device_devn(const void* in, void* out, const int32_t* n_live, i
                          n_live);
 }
 
+static_assert(SCAN_NOALLOC_SCRATCH_BYTES == sca::kNoAllocScratchBytes,
+              "the header states the static scratch size");
+
+scan_status scan_device_noalloc(const void* in, void* out, int64_t n, scan_dtype dtype,
+                                scan_op op, void* stream) {
+  sca::Fmt fmt;
+  size_t eb;
+  if (!fmt_of(dtype, &fmt, &eb)) return SCAN_ENOTSUP;
+  if (fmt == sca::Fmt::F16 || fmt == sca::Fmt::BF16) return SCAN_ENOTSUP;
+  const int opi = op_index(op);
+  if (opi < 0 || opi > 2) return SCAN_ENOTSUP;
+  if (n < 0 || n > kMaxN) return SCAN_EINVAL;
+  // the static scratch bounds n: rejected before any pointer is looked at
+  if (scan_device_scratch_bytes(n, dtype) > SCAN_NOALLOC_SCRATCH_BYTES) return SCAN_ESCRATCH;
+  if (n == 0) return SCAN_OK;
+  if (in == nullptr || out == nullptr) return SCAN_EINVAL;
+  if (!aligned(in, eb) || !aligned(out, eb)) return SCAN_EINVAL;
+  const size_t bytes = (size_t)n * eb;
+  if (overlap(in, bytes, out, bytes)) return SCAN_EALIAS;
+  void* scratch = nullptr;
+  const hipError_t e = sca::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(sca::launch_scan_device(in, out, n, fmt, opi, false, scratch,
+                                            (hipStream_t)stream));
+}
+
 scan_status scan_device_inclusive(const void* in, void* out, int64_t n, scan_dtype dtype,
                                   scan_op op, void* scratch, size_t scratch_bytes,
                                   void* stream) {

@@ -68,4 +68,10 @@ inline uint64_t* desc_base(void* scratch) {
 }
 hipError_t launch_fill_desc(uint64_t* desc, int64_t ntiles, int words, hipStream_t stream);
 
+// The allocation-free device scan keeps its descriptors in a static device
+// array of this many bytes per GPU; noalloc_scratch() returns the current
+// device's copy (hipGetSymbolAddress, once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace sca

@@ -26,8 +26,19 @@
 // The waves meet through an LDS counter and flag (no barrier), so the
 // look-back never holds up the data waves' loads and scans; one barrier then
 // hands the prefix back, with the data waves asleep in it.
+#include <atomic>
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
+
+// Scratch of the allocation-free entry point: one copy of this array per GPU,
+// held until the process ends and shared by every such call on that GPU (so
+// two of them in flight at once on one GPU race).  In host code the name
+// `scratch` denotes a host-side stand-in, not a device address: host code
+// only ever uses the address hipGetSymbolAddress returns for the current
+// device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[sca::kNoAllocScratchBytes];
 
 namespace sca {
 
@@ -280,6 +291,34 @@ hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int
     case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream, n_dev);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Device address of the calling thread's current GPU's copy of `scratch`,
+// looked up once per device (with that device current) and kept.
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

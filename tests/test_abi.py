@@ -277,3 +277,22 @@ def test_devn_validation():
                                  None) == EINVAL
     assert L.select_compact_devn(A, S + 0x10000, B, B + 0x10000, B + 0x10000, cap, 4, S, cneed,
                                  None) == EALIAS                        # the count is num_out
+
+
+def test_scan_device_noalloc_validation():
+    # every case is rejected on the host, before the static scratch is looked up
+    L = sc.lib()
+    assert L.scan_device_noalloc(A, B, 100, D["f16"], OP["add"], None) == ENOTSUP
+    assert L.scan_device_noalloc(A, B, 100, D["i32"], OP["mul"], None) == ENOTSUP
+    assert L.scan_device_noalloc(A, B, -1, D["i32"], OP["add"], None) == EINVAL
+    assert L.scan_device_noalloc(A, B, 0, D["i32"], OP["add"], None) == OK
+    assert L.scan_device_noalloc(0, B, 100, D["i32"], OP["add"], None) == EINVAL
+    assert L.scan_device_noalloc(A + 2, B, 100, D["i32"], OP["add"], None) == EINVAL
+    assert L.scan_device_noalloc(A, A + 8, 100, D["i32"], OP["add"], None) == EALIAS
+    # the static scratch holds the descriptors of at most 65,535 tiles of 7,168 elements
+    n_max = 65_535 * 7_168
+    assert L.scan_device_scratch_bytes(n_max, D["i32"]) <= 8 << 20
+    assert L.scan_device_scratch_bytes(n_max + 1, D["i32"]) > 8 << 20
+    for dt in ("i32", "f64"):
+        assert L.scan_device_noalloc(A, B, n_max + 1, D[dt], OP["add"], None) == ESCRATCH
+        assert L.scan_device_noalloc(A, B, (1 << 31) - 1, D[dt], OP["min"], None) == ESCRATCH
