@@ -84,7 +84,7 @@ KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (
     "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, false, 4, 11, 12>(": ("dev_i32_add",
                                                                               "scan_device"),
     "void sca::reduce_partials_kernel<sca::FmtI32, (sca::Op)0, 4, 16>(": ("reduce_i32_add", "reduce"),
-    "void sca::reduce_by_key_kernel<sca::FmtU32, sca::FmtF32, 4, 15, 8>(": ("reduce_by_key",
+    "void sca::reduce_by_key_kernel<sca::FmtU32, sca::FmtF32, 4, 11, 6, 3, 6>(": ("reduce_by_key",
                                                                          "reduce_by_key"),
     "void sca::select_kernel<4, true, 8, 8>(": ("select_p0.5", "select"),
     "void sca::radix_scatter_kernel<unsigned int, (sca::KeyKind)0, 0, 8, 16, true>(": ("sort_u32",

@@ -31,9 +31,9 @@
 
 namespace sca {
 
-// Smallest tile (in vectors) of any launch shape below (15 data waves x 8
+// Smallest tile (in vectors) of any launch shape below (11 data waves x 6
 // loads x 64 lanes); scratch is sized for it.
-constexpr int64_t kRbkMinTileVecs = 7680;
+constexpr int64_t kRbkMinTileVecs = 4224;
 
 // The scan state of a span: run starts in it and the sum after the last one.
 // V is float for f32 values and uint32_t for i32/u32 values (wrapping).
@@ -90,8 +90,10 @@ __device__ __forceinline__ uint32_t key_at(uintptr_t k_base, int64_t i, int64_t 
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(b.r, 0, 0, 0);
 }
 
-template <class KF, class VF, int E, int WD, int K>
-__global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
+// FL: loads per flush of the run outputs staged in LDS; MINW: the waves per
+// SIMD the register allocation must allow (two workgroups per CU).
+template <class KF, class VF, int E, int WD, int K, int FL, int MINW>
+__global__ __launch_bounds__(64 * (WD + 1), MINW) void reduce_by_key_kernel(
     uintptr_t k_base, uintptr_t v_base, int64_t n_cap, const int32_t* n_dev, int64_t ph,
     uintptr_t keys_out, uintptr_t values_out, uintptr_t num_runs, uint64_t* desc) {
   using V = typename ValT<VF>::V;
@@ -106,6 +108,10 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
   __shared__ W s_prefix;
   __shared__ uint32_t s_posted;
   __shared__ uint32_t s_agg_done;
+  // run outputs of FL loads per data wave (at most 64 lanes x E run starts a load)
+  static_assert(K % FL == 0, "whole flushes");
+  __shared__ uint32_t s_emit_k[WD][kWave * E * FL];
+  __shared__ V s_emit_v[WD][kWave * E * FL];
 
   const int lane = lane_id(), wave = wave_id();
   const int64_t tile = blockIdx.x;
@@ -244,14 +250,32 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
     W carry = s_prefix;
     for (int w = 0; w < wave; ++w) carry = combine<Op::Add>(carry, s_wave[w]);
     // With the exclusive state st of a run-starting element: its key opens
-    // run st.c, and run st.c - 1 (if any) closed with sum st.s.  (Run indices
-    // never reach n; the bound only keeps every store inside the caller's
+    // run st.c, and run st.c - 1 (if any) closed with sum st.s.  The element
+    // writes both to slot st.c - base of the wave's LDS staging area, and
+    // after every FL loads the wave stores the slots it filled as contiguous
+    // runs of keys_out and values_out (consecutive lanes at consecutive
+    // addresses) rather than one scattered store per run start.  (Run indices never
+    // reach n; the bound only keeps every store inside the caller's
     // n-element outputs whatever the input.)
-    auto emit = [&](const W& st, uint32_t key) {
-      if (st.c < (uint64_t)n) {
-        *gptr<uint32_t>(keys_out + (uintptr_t)st.c * 4) = key;
-        if (st.c > 0) *gptr<V>(values_out + (uintptr_t)(st.c - 1) * 4) = st.s;
+    uint32_t* const sk = s_emit_k[wave];
+    V* const sv = s_emit_v[wave];
+    uint32_t base = carry.c;                           // run index of slot 0
+    auto flush = [&](uint32_t upto) {                  // upto: runs opened so far (wave-uniform)
+      const uint32_t cnt = upto - base;
+      // a wave's LDS operations complete in order; keep the compiler from
+      // moving the reads of other lanes' slots above the writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (uint32_t i = (uint32_t)lane; i < cnt; i += kWave) {
+        const uint64_t c = (uint64_t)base + i;
+        if (c < (uint64_t)n) *gptr<uint32_t>(keys_out + (uintptr_t)c * 4) = sk[i];
+        if (c > 0 && c - 1 < (uint64_t)n) *gptr<V>(values_out + (uintptr_t)(c - 1) * 4) = sv[i];
       }
+      base = upto;
+    };
+    auto stage = [&](const W& st, uint32_t key) {
+      const uint32_t slot = st.c - base;
+      sk[slot] = key;
+      sv[slot] = st.s;
     };
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
 #pragma unroll
         for (int k = 0; k < E; ++k) {
           const uint32_t h = (h4 >> k) & 1u;
-          if (h) emit(st, elem<E>(rk[j], k));
+          if (h) stage(st, elem<E>(rk[j], k));
           st = combine<Op::Add>(st, W(h, __builtin_bit_cast(V, elem<E>(rv, k))));
         }
       } else {
@@ -280,7 +304,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
         for (int k = 0; k < E; ++k) {
           const int64_t i = (jv + lane) * E + k;
           const uint32_t h = (h4 >> k) & 1u;
-          if (h) emit(st, elem<E>(rk[j], k));
+          if (h) stage(st, elem<E>(rk[j], k));
           st = combine<Op::Add>(st, W(h, value(rv, k, i)));
           // the last element closes the last run
           if (i == hi - 1 && st.c >= 1 && st.c <= (uint64_t)n) {
@@ -289,6 +313,7 @@ __global__ __launch_bounds__(64 * (WD + 1)) void reduce_by_key_kernel(
           }
         }
       }
+      if ((j + 1) % FL == 0 && carry.c != base) flush(carry.c);
     }
   } else {
     // ---- look-back wave ----
@@ -357,7 +382,7 @@ static int64_t rbk_tiles_for(int64_t n, int e, int64_t tv) {
 // Sized for the one-element-per-vector path and the smallest tile.
 size_t reduce_by_key_tiles(int64_t n) { return (size_t)rbk_tiles_for(n, 1, kRbkMinTileVecs); }
 
-template <class KF, class VF, int WD, int K>
+template <class KF, class VF, int WD, int K, int FL, int MINW>
 static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* keys_out,
                                  void* values_out, int32_t* num_runs, int64_t n, void* scratch,
                                  hipStream_t stream, const int32_t* n_dev) {
@@ -373,10 +398,10 @@ static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* key
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ko = (uintptr_t)keys_out, vo = (uintptr_t)values_out, nr = (uintptr_t)num_runs;
   if (vec) {
-    reduce_by_key_kernel<KF, VF, 4, WD, K><<<grid, block, 0, stream>>>(
+    reduce_by_key_kernel<KF, VF, 4, WD, K, FL, MINW><<<grid, block, 0, stream>>>(
         ka - ph * 4, va - ph * 4, n, n_dev, ph, ko, vo, nr, desc);
   } else {
-    reduce_by_key_kernel<KF, VF, 1, WD, K><<<grid, block, 0, stream>>>(
+    reduce_by_key_kernel<KF, VF, 1, WD, K, FL, MINW><<<grid, block, 0, stream>>>(
         ka, va, n, n_dev, 0, ko, vo, nr, desc);
   }
   return hipGetLastError();
@@ -387,11 +412,14 @@ static hipError_t launch_rbk_t(const void* keys, const void* values, void* keys_
                                void* values_out, int32_t* num_runs, int64_t n, void* scratch,
                                hipStream_t stream, const int32_t* n_dev) {
   // Launch shape measured on MI355X over 2^27 pairs in runs of mean length 8
-  // (us): 15 data waves x 8 loads 303.4, 7 x 16 314.4, 15 x 6 314.4,
-  // 7 x 8 332.8, 9 x 12 350.7.  With the keys held and the values streamed,
-  // larger tiles (fewer links in the look-back chain) win.
-  return launch_rbk_cfg<KF, VF, 15, 8>(keys, values, keys_out, values_out, num_runs, n, scratch,
-                                       stream, n_dev);
+  // (us, u32 values): 11 data waves x 6 loads with two workgroups per CU and
+  // the run outputs flushed every 3 loads 252-255; every 1 / 2 loads 273-277 /
+  // 263; once per wave (132 KiB of LDS, one workgroup per CU) 320.  7 x 8 (2
+  // loads per flush) 263, 15 x 8 (one workgroup per CU) 276-281, 11 x 4
+  // 277, 13 x 6 283 (20 bytes spilled).  The earlier kernel, with one
+  // scattered store per run start: 15 x 8 285-294, 11 x 8 at two per CU 277-281.
+  return launch_rbk_cfg<KF, VF, 11, 6, 3, 6>(keys, values, keys_out, values_out, num_runs, n,
+                                             scratch, stream, n_dev);
 }
 
 template <class KF>

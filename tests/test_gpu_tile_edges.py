@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 # launch shapes (vectors per tile)
 DEV_TILE_VECS = 11 * 12 * 64     # device scans: 11 data waves x 12 loads
 SEL_TILE_VECS = 8 * 8 * 4 * 64   # select: 8 data waves x 8 chunks x 4 loads
-RBK_TILE_VECS = 15 * 8 * 64      # reduce-by-key: 15 data waves x 8 loads
+RBK_TILE_VECS = 11 * 6 * 64      # reduce-by-key: 11 data waves x 6 loads
 
 
 def edge_sizes(t, ph=0):
