@@ -29,8 +29,10 @@
 //      two chunks in flight: ranks within the chunk come from DPP scans of the
 //      lane counts; the selected elements are packed into the wave's own LDS
 //      staging area at their rank, shifted so LDS vectors line up with the
-//      vectors of `out`, and the wave stores the chunk's run with whole-vector
-//      stores (element stores only for the partial vectors at its two ends).
+//      vectors of `out`, and the wave stores the whole 128-byte lines the
+//      chunk completed with whole-vector stores; the unfinished line is
+//      carried in LDS into the next chunk, so a wave writes partial vectors
+//      and lines (element by element) only at the two ends of its output.
 //      Unselected elements are written to a per-lane discard slot, and stores
 //      without data point past the buffer's end, so every chunk issues the
 //      same instructions whatever the flags hold.
@@ -115,8 +117,10 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   constexpr int64_t kWaveVecs = kChunkVecs * C;
   constexpr int64_t kTileVecs = kWaveVecs * WD;
   static_assert(kTileVecs >= kSelMinTileVecs, "scratch is sized for the smallest tile");
-  // staging slots per wave: one chunk of elements plus the shift of its start
-  constexpr int kStage = (int)kChunkVecs * E + E;
+  // staging slots per wave: one chunk of elements plus the unfinished line
+  // carried from the previous chunk (or the slots before the wave's first
+  // output position in its first line), fewer than 128 bytes
+  constexpr int kStage = (int)kChunkVecs * E + 128 / EB;
   constexpr int kStageVecs = kStage / E;
   constexpr int kStoreIters = (kStageVecs + kWave - 1) / kWave;
   __shared__ __attribute__((aligned(16))) T s_stage[WD][kStage];
@@ -276,15 +280,27 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   __syncthreads();
   if (wave >= WD) return;
 
-  // 3. stream the chunks: rank, pack into LDS, store the run
-  uint32_t r0 = s_prefix;                    // output index of the chunk's first selected element
+  // 3. stream the chunks: rank, pack into LDS, store the run.  The wave's
+  // LDS staging area starts at a 128-byte line of `out` (slot 0 is the
+  // element at window position `base`), and every chunk stores only the
+  // whole lines it has completed; the partial line at the end moves to the
+  // front of the staging area and is completed by the next chunk.  So the
+  // wave writes whole lines except at the two ends of its output range.
+  constexpr int LE = 128 / EB;                        // elements per 128-byte line
+  static_assert(LE % E == 0, "a line is whole vectors");
+  uint32_t r0 = s_prefix;                             // output index of the wave's first selected element
   for (int w = 0; w < wave; ++w) r0 += s_wave[w];
   r0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);   // wave-uniform: buffer bases use it
   T* const stage = s_stage[wave];
+  // window position P lies at a line start when (out_base + P * EB) % 128 == 0
+  const int lphase = (int)((out_base % 128) / EB);
+  const int64_t p_valid = (int64_t)r0 + out_ph;       // the wave's first output position
+  int64_t base = p_valid - (p_valid + lphase) % LE;   // line-aligned position of slot 0
+  int fill = (int)(p_valid - base);                   // slot of the next kept element
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     if (c + 2 < C) load_chunk(c + 2);
-    const int s = (int)(((int64_t)r0 + out_ph) % E);   // stage slot of the first element
+    const int s = fill;
     // ranks: the chunk's elements are ordered load by load, then lane by
     // lane.  The lane's J counts (at most E each) are packed in bytes and
     // scanned exclusively in one pass: a byte then sums at most 63 lanes'
@@ -333,33 +349,55 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
     // a wave's LDS operations complete in order; wait for the writes before
     // the reads of other lanes' slots
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // store stage vectors [0, nvec) to output vectors g0 + q
-    const int64_t g0 = ((int64_t)r0 + out_ph) / E;
-    const int nvec = (end + E - 1) / E;
-    const Buf ob(out_base + g0 * VB, (int64_t)nvec * VB);
+    // store slots [first, cut): whole lines, or everything at the wave's last
+    // chunk; slots below the wave's first output position are not its own
+    const int cut = c == C - 1 ? end : end / LE * LE;
+    const int first = (int)(p_valid > base ? p_valid - base : 0);
+    const int nvec = (cut + E - 1) / E;
+    const Buf ob(out_base + (base / E) * VB, (int64_t)nvec * VB);
 #pragma unroll
     for (int i = 0; i < kStoreIters; ++i) {
       const int q = lane + i * kWave;
-      const bool full = q * E >= s && (q + 1) * E <= end;
+      const bool full = q * E >= first && (q + 1) * E <= cut;
       const int qr = q < kStageVecs ? q : kStageVecs - 1;
       const V v = *(const V*)&stage[qr * E];
       sel_store<VB>(v, ob.r, full ? (uint32_t)(q * VB) : kOffNone);
     }
     // the partial vectors: the first (lane 0) and the last (lane 1), element by element
     {
-      const int q = lane == 0 ? 0 : nvec - 1;
-      const bool partial = (lane == 0 || (lane == 1 && nvec > 1)) && nvec > 0 &&
-                           !(q * E >= s && (q + 1) * E <= end);
+      const int q = lane == 0 ? first / E : nvec - 1;
+      const bool partial = (lane == 0 || (lane == 1 && nvec - 1 != first / E)) && cut > first &&
+                           !(q * E >= first && (q + 1) * E <= cut);
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         const int slot = q * E + k;
-        const bool ok = partial && slot >= s && slot < end;
+        const bool ok = partial && slot >= first && slot < cut;
         const T v = stage[ok ? slot : 0];
         const uint32_t off = ok ? (uint32_t)(slot * EB) : kOffNone;
         sel_store<EB>(v, ob.r, off);
       }
     }
-    r0 += (uint32_t)(end - s);
+    // the unfinished line moves to the front (fewer than LE slots, read from
+    // slot cut >= LE on, so source and destination never overlap)
+    if (c < C - 1 && cut > 0) {
+      const int cnt = end - cut;
+      constexpr int kMoveIters = (LE + kWave - 1) / kWave;
+      T t[kMoveIters];
+#pragma unroll
+      for (int i = 0; i < kMoveIters; ++i) {
+        const int q = lane + i * kWave;
+        t[i] = stage[q < cnt ? cut + q : 0];
+      }
+#pragma unroll
+      for (int i = 0; i < kMoveIters; ++i) {
+        const int q = lane + i * kWave;
+        if (q < cnt) stage[q] = t[i];
+      }
+      base += cut;
+      fill = cnt;
+    } else {
+      fill = end;
+    }
   }
 }
 
