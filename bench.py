@@ -81,7 +81,7 @@ def sources_sha(kind):
 KERNEL_KEYS = {                 # kernel-name prefix in the profiler output -> (workload, sources)
     "void sca::scan_rows_kernel<sca::FmtBF16, (sca::Op)0, true, 8, 4, 4>(": ("rows_bf16_excl",
                                                                            "scan_rows"),
-    "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, false, 4, 11, 12>(": ("dev_i32_add",
+    "void sca::scan_device_kernel<sca::FmtI32, (sca::Op)0, false, 4, 8, 16>(": ("dev_i32_add",
                                                                               "scan_device"),
     "void sca::reduce_partials_kernel<sca::FmtI32, (sca::Op)0, 4, 16>(": ("reduce_i32_add", "reduce"),
     "void sca::reduce_by_key_kernel<sca::FmtU32, sca::FmtF32, 4, 11, 6, 3, 6>(": ("reduce_by_key",

@@ -6,19 +6,30 @@
 // of that page's PrefixSumExecutor section, here out of place and for every
 // dtype and op): the same kernel with a different store stage.
 //
-// Workgroup b owns tile b.  It has WD data waves and one look-back wave.
-//  - Each data wave loads its run of 64*K 16-byte vectors (load j of lane l
-//    is vector j*64 + l of the run, so every load instruction covers 1 KiB),
-//    scans every vector lane-serially and the 64 lane totals with a DPP wave
-//    scan, and posts its wave total to LDS; the last data wave to post
-//    publishes the tile's aggregate at once.
+// Workgroup b owns tile b: data waves that load, scan and store it, and one
+// look-back wave.  Two tile layouts, chosen per operation (launcher below):
+//  - side by side (scan_device_kernel): 8 data waves x 16 loads; load j of
+//    lane l in wave w is vector (j*8 + w)*64 + l of the tile, so load round j
+//    of all data waves reads one aligned 8 KiB stretch.  Each wave scans every
+//    vector lane-serially and the 64 lane totals with a DPP wave scan, and
+//    posts each load's total to an LDS table (load q = j*8 + w at slot q);
+//    the last data wave to post scans the table (two slots per lane), which
+//    gives every load the combine of the loads before it and the tile's
+//    aggregate, and publishes the aggregate at once.
+//  - runs (scan_device_runs_kernel): 11 data waves x 12 loads; each data wave
+//    loads its own run of 64*12 vectors (load j of lane l is vector j*64 + l
+//    of the run), scans it with a running carry, and posts its wave total;
+//    the last data wave to post publishes the tile's aggregate.  More data
+//    waves per CU hide the longer dependent chains of a compare-and-select
+//    combine.
+// In both:
 //  - The look-back wave starts walking back over the predecessors'
 //    descriptors as soon as the workgroup starts, while the data is still in
 //    flight: the walk needs nothing from this tile.  When the walk ends and
 //    the aggregate is out, it publishes the tile's inclusive prefix and hands
 //    the exclusive prefix to the data waves through LDS.
-//  - The data waves then combine tile prefix, earlier waves, earlier vectors
-//    and earlier elements of the vector, and store.
+//  - The data waves then combine tile prefix, what precedes their load or run
+//    in the tile and earlier elements of the vector, and store.
 // The input is read once and the output written once.  Tile ids are the
 // workgroup ids: no atomic counter (a device-wide atomic on one address
 // serializes at about 11 ns per tile on MI355X); the look-back's bounded wait
@@ -42,12 +53,197 @@ static __device__ __align__(256) uint8_t scratch[sca::kNoAllocScratchBytes];
 
 namespace sca {
 
-// Scratch is sized for tiles of at least this many vectors (7 x 16 x 64; the
-// launch shape below, 11 data waves x 12 loads x 64 lanes, has 8448).
+// Scratch is sized for tiles of at least this many vectors (the launch
+// shapes below have 8 x 16 x 64 = 8192 and 11 x 12 x 64 = 8448).
 constexpr int64_t kDevMinTileVecs = 7168;
 
 template <class F, Op O, bool INCL, int E, int WD, int K>
 __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_kernel(
+    uintptr_t in_base, uintptr_t out_base, int64_t n_cap, const int32_t* n_dev, int64_t ph,
+    uint64_t* desc) {
+  using S = typename F::S;
+  using W = typename F::W;
+  using IO = VecIO<S, E>;
+  constexpr int64_t VB = (int64_t)E * sizeof(S);       // bytes per vector
+  constexpr int kQ = WD * K;                           // loads per tile
+  constexpr int64_t kTileVecs = (int64_t)kWave * kQ;
+  static_assert(kTileVecs >= kDevMinTileVecs, "scratch is sized for the smallest tile");
+  static_assert(kQ == 2 * kWave, "the table of load totals is two slots per lane");
+  __shared__ W s_tot[kQ];         // total of load q
+  __shared__ W s_pre[kQ];         // combine of loads 0 .. q-1
+  __shared__ W s_agg;             // the tile's aggregate
+  __shared__ W s_prefix;          // the tile's exclusive prefix
+  __shared__ uint32_t s_posted;   // data waves whose totals are in s_tot
+  __shared__ uint32_t s_agg_done; // s_pre and s_agg are written, the aggregate is published
+
+  const int lane = lane_id(), wave = wave_id();
+  const int64_t tile = blockIdx.x;
+  const W id = identity<O, W>();
+  const int64_t n = live_count(n_cap, n_dev);
+  const int64_t lo = ph, hi = n + ph, v_last = (hi - 1) / E;
+  const int64_t tb = tile * kTileVecs;                 // the tile's first vector
+  if (n == 0 || tb > v_last) return;                   // past the live count: nothing to do
+  if (threadIdx.x == 0) {
+    s_posted = 0u;
+    s_agg_done = 0u;
+  }
+  __syncthreads();
+
+  // Tile t's input, bounded at its last valid vector (zero bits past v_last).
+  auto tile_buf = [&](int64_t t) {
+    const int64_t left = v_last + 1 - t * kTileVecs;
+    const int64_t nv = left <= 0 ? 0 : (left < kTileVecs ? left : kTileVecs);
+    return Buf(in_base + t * kTileVecs * VB, nv * VB);
+  };
+  // Elements of a load whose first vector is jv, with the identity outside [lo, hi).
+  auto unpack = [&](int64_t jv, const typename IO::Raw& r, W (&x)[E]) {
+    if (jv * E >= lo && (jv + kWave) * E <= hi) {       // wave-uniform: all vectors full
+      IO::template unpack<F>(r, x);
+    } else {
+      IO::template unpack_masked<F>(r, (jv + lane) * E, lo, hi, id, x);
+    }
+  };
+  // Lane-serial scan of a load's vectors, then the wave scan of the lane
+  // totals; returns the inclusive wave scan.
+  auto scan_load = [&](W (&x)[E]) -> W {
+#pragma unroll
+    for (int k = 1; k < E; ++k) x[k] = combine<O>(x[k - 1], x[k]);
+    return wave_scan_incl<O>(x[E - 1]);
+  };
+  // Scan of the table of load totals in load order, lane l holding loads 2l
+  // and 2l+1; returns the inclusive scan of the pairs (lane 63: the tile's
+  // aggregate).  The fallback below reduces a tile with this same grouping.
+  auto scan_pairs = [&](W a, W b) -> W { return wave_scan_incl<O>(combine<O>(a, b)); };
+
+  if (wave < WD) {
+    // ---- data wave ----
+    const Buf buf = tile_buf(tile);
+    typename IO::Raw raw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      raw[j] = IO::load(buf, (uint32_t)(((j * WD + wave) * kWave + lane) * VB));
+    // x[j][k] ends as the combine of load j's elements before element k of
+    // the lane's vector (exclusive) or up to it (inclusive), computed in place
+    // so that only the tile's own data stays live across the barrier; lane j
+    // collects load j's total
+    W x[K][E];
+    W tot = id;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      unpack(tb + (j * WD + wave) * kWave, raw[j], x[j]);
+      const W incl = scan_load(x[j]);
+      const W pre = wave_shift_excl<O>(incl);
+      const W t = readlane(incl, kWave - 1);
+      if (lane == j) tot = t;
+      if constexpr (INCL) {
+#pragma unroll
+        for (int k = 0; k < E; ++k) x[j][k] = combine<O>(pre, x[j][k]);
+      } else {
+#pragma unroll
+        for (int k = E - 1; k > 0; --k) x[j][k] = combine<O>(pre, x[j][k - 1]);
+        x[j][0] = pre;
+      }
+#pragma unroll
+      for (int k = 0; k < E; ++k) materialize(x[j][k]);
+    }
+    if (lane < K) s_tot[lane * WD + wave] = tot;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    uint32_t before = 0;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(&s_posted, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before == (uint32_t)WD - 1) {
+      // the last data wave to post: every load total is in the table
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const W a = s_tot[2 * lane], b = s_tot[2 * lane + 1];
+      const W sp = scan_pairs(a, b);
+      const W e = wave_shift_excl<O>(sp);
+      s_pre[2 * lane] = e;
+      s_pre[2 * lane + 1] = combine<O>(e, a);
+      const W agg = readlane(sp, kWave - 1);
+      if (lane == 0) {
+        s_agg = agg;
+        if (tile > 0) Desc<W>::publish(desc, tile, kAgg, agg);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0)
+        __hip_atomic_store(&s_agg_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();  // sleeps in hardware until the look-back wave has the prefix
+    const W tp = s_prefix;
+    if (tb * E >= lo && (tb + kTileVecs) * E <= hi) {   // tile-uniform: all vectors full
+      // one buffer per load, so every store takes the lane's offset alone
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int q = j * WD + wave;
+        const W p = combine<O>(tp, s_pre[q]);
+        const Buf ob(out_base + (tb + q * kWave) * VB, kWave * VB);
+        W y[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(p, x[j][k]);
+        IO::template store_full<F>(ob, (uint32_t)(lane * VB), y);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int q = j * WD + wave;
+        const W p = combine<O>(tp, s_pre[q]);
+        W y[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) y[k] = combine<O>(p, x[j][k]);
+        const int64_t v = tb + q * kWave + lane;
+        if (v <= v_last) IO::template store<F>(out_base, v, lo, hi, y);
+      }
+    }
+  } else {
+    // ---- look-back wave ----
+    W prefix = id;
+    if (tile > 0) {
+      // fallback for a late predecessor: reduce its input with the grouping
+      // its own data waves use (each load scanned alone, then the table of
+      // load totals scanned in pairs), so the result is bit for bit the
+      // aggregate that tile would publish, floating add included; a few loads
+      // at a time (this rare path must not raise the kernel's register count,
+      // which sets how many workgroups fit on a CU)
+      auto reduce_tile = [&](int64_t t) -> W {
+        constexpr int kG = 4;
+        static_assert(kQ % kG == 0, "whole groups of loads");
+        const Buf buf = tile_buf(t);
+        W a = id, b = id;   // lane l: totals of loads 2l and 2l+1
+#pragma unroll 1
+        for (int g = 0; g < kQ / kG; ++g) {
+          typename IO::Raw r[kG];
+#pragma unroll
+          for (int i = 0; i < kG; ++i)
+            r[i] = IO::load(buf, (uint32_t)(((g * kG + i) * kWave + lane) * VB));
+#pragma unroll
+          for (int i = 0; i < kG; ++i) {
+            const int q = g * kG + i;
+            W y[E];
+            unpack(t * kTileVecs + q * kWave, r[i], y);
+            const W tq = readlane(scan_load(y), kWave - 1);
+            if (lane == (q >> 1)) {
+              if (i & 1) b = tq;
+              else a = tq;
+            }
+          }
+        }
+        return readlane(scan_pairs(a, b), kWave - 1);
+      };
+      prefix = look_back<O, W, kPollLong>(desc, tile, kLookBackTimeout, reduce_tile);
+    }
+    while (!lds_flag_set(&s_agg_done)) __builtin_amdgcn_s_sleep(1);
+    if (lane == 0) {
+      Desc<W>::publish(desc, tile, kInc, combine<O>(prefix, s_agg));
+      s_prefix = prefix;
+    }
+    __syncthreads();
+  }
+}
+
+// The runs layout (contiguous run of 64*K vectors per data wave).
+template <class F, Op O, bool INCL, int E, int WD, int K>
+__global__ __launch_bounds__(64 * (WD + 1)) void scan_device_runs_kernel(
     uintptr_t in_base, uintptr_t out_base, int64_t n_cap, const int32_t* n_dev, int64_t ph,
     uint64_t* desc) {
   using S = typename F::S;
@@ -227,12 +423,30 @@ size_t scan_device_tiles(int64_t n, Fmt fmt) {
   return (size_t)tiles_for(n, 1, kDevMinTileVecs);
 }
 
-// One launch shape: WD data waves (plus the look-back wave), K vectors per
-// lane per tile.
-template <class F, Op O, bool INCL, int WD, int K>
+// Tile layout by operation, measured on MI355X (us per exclusive scan; runs
+// 11 x 12 against side by side 8 x 16): i32 add 2^28 367.9 / 363.3, f32 add
+// 2^27 191.7 / 188.8, i64 add 2^26 198.8 / 196.0, f64 add 2^26 198.3 /
+// 195.7; u32 max 2^27 190.3 / 189.1; f32 min 2^27 190.5 / 195.3, f32 max
+// 2^27 190.0 / 196.3, i64 min 2^26 195.5 / 202.6, i64 max 2^26 195.7 /
+// 202.0.  Side by side, a load round of the data waves covers one aligned
+// 8 KiB stretch, which a copy that holds its data until a barrier moves
+// faster (6.2 TB/s against 5.7 for 8 KiB runs); but it has 8 data waves per
+// workgroup against 11, and a combine that is a compare and a select (min and
+// max of floats, which keep the later of two equal values, and of 64-bit
+// integers) makes every DPP step three instructions, which then stall the
+// fewer waves.  Add takes the side-by-side tiles, min and max the runs (the
+// 32-bit integer min/max tie, and side by side their inclusive forms need
+// more registers than two workgroups per CU allow).
+template <Op O>
+constexpr bool kSideBySide = O == Op::Add;
+
+template <class F, Op O, bool INCL>
 static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
                                  hipStream_t stream, const int32_t* n_dev) {
   using S = typename F::S;
+  constexpr bool kSide = kSideBySide<O>;
+  constexpr int WD = kSide ? 8 : 11;    // data waves (plus the look-back wave)
+  constexpr int K = kSide ? 16 : 12;    // loads per lane
   constexpr int EV = 16 / (int)sizeof(S);
   constexpr int64_t TV = (int64_t)kWave * WD * K;
   const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
@@ -244,29 +458,28 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   hipError_t err = launch_fill_desc(desc, ntiles, Desc<typename F::W>::kWords, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
-  if (vec) {
-    scan_device_kernel<F, O, INCL, EV, WD, K><<<grid, block, 0, stream>>>(
-        ia - ph * sizeof(S), oa - ph * sizeof(S), n, n_dev, ph, desc);
+  const uintptr_t ib = vec ? ia - ph * sizeof(S) : ia, ob = vec ? oa - ph * sizeof(S) : oa;
+  if constexpr (kSide) {
+    if (vec)
+      scan_device_kernel<F, O, INCL, EV, WD, K><<<grid, block, 0, stream>>>(ib, ob, n, n_dev, ph, desc);
+    else
+      scan_device_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ib, ob, n, n_dev, 0, desc);
   } else {
-    scan_device_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ia, oa, n, n_dev, 0,
-                                                                        desc);
+    if (vec)
+      scan_device_runs_kernel<F, O, INCL, EV, WD, K><<<grid, block, 0, stream>>>(ib, ob, n, n_dev, ph,
+                                                                               desc);
+    else
+      scan_device_runs_kernel<F, O, INCL, 1, WD, K><<<grid, block, 0, stream>>>(ib, ob, n, n_dev, 0,
+                                                                              desc);
   }
   return hipGetLastError();
 }
 
-// Launch shape measured on MI355X (us per scan; i32 add over 2^28 / i64 min
-// over 2^26): 11 data waves x 12 loads (132 KiB tiles) 365.8 / 208.3,
-// 7 x 16: 374.2 / 215.4 (3 workgroups per CU; 368.2 when capped at 2),
-// 7 x 20: 369.6, 8 x 16: 370.4 / 292.3, 15 x 8: 424.0 / 264.4.  An earlier
-// sweep over 3 and 4 data waves was slower still (3 x 16: 436).  Few, large
-// tiles win, since each look-back costs microseconds of latency; but more
-// resident tiles per CU (a wider address window in flight) lose, so the
-// shape is also chosen for two workgroups per CU.
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, bool incl, void* scratch,
                                hipStream_t stream, const int32_t* n_dev) {
-  return incl ? launch_dev_cfg<F, O, true, 11, 12>(in, out, n, scratch, stream, n_dev)
-              : launch_dev_cfg<F, O, false, 11, 12>(in, out, n, scratch, stream, n_dev);
+  return incl ? launch_dev_cfg<F, O, true>(in, out, n, scratch, stream, n_dev)
+              : launch_dev_cfg<F, O, false>(in, out, n, scratch, stream, n_dev);
 }
 
 template <class F>

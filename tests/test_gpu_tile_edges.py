@@ -29,7 +29,8 @@ from parity import FP_ABS, FP_REL, check_exact, check_fp_add
 pytestmark = pytest.mark.gpu
 
 # launch shapes (vectors per tile)
-DEV_TILE_VECS = 11 * 12 * 64     # device scans: 11 data waves x 12 loads
+DEV_ADD_TILE_VECS = 8 * 16 * 64  # device add scans: 8 side-by-side data waves x 16 loads
+DEV_RUNS_TILE_VECS = 11 * 12 * 64  # device min/max scans: 11 data waves x 12 loads each
 SEL_TILE_VECS = 8 * 8 * 4 * 64   # select: 8 data waves x 8 chunks x 4 loads
 RBK_TILE_VECS = 11 * 6 * 64      # reduce-by-key: 11 data waves x 6 loads
 
@@ -54,6 +55,10 @@ def views(n, dt, off_in, off_out):
     return big_in, big_out, big_in[off_in:off_in + n], big_out[off_out:off_out + n]
 
 
+def dev_tile_vecs(op):
+    return DEV_ADD_TILE_VECS if op == "add" else DEV_RUNS_TILE_VECS
+
+
 def compare(gpu, x, dt, op, inclusive, label):
     if op == "add" and dt in oracle.FLOATS:
         ora, ref, absref = oracle.scan(x, dt, op, exclusive=not inclusive, want_ref=True)
@@ -66,15 +71,15 @@ def compare(gpu, x, dt, op, inclusive, label):
 # device-wide scans (exclusive and inclusive), every element width
 # ---------------------------------------------------------------------------
 
-DEV_CASES = [("i32", "add"), ("u32", "max"), ("f32", "min"), ("f32", "add"), ("i64", "add"),
-             ("u64", "min"), ("f64", "max")]
+DEV_CASES = [("i32", "add"), ("u32", "max"), ("i32", "min"), ("f32", "min"), ("f32", "add"),
+             ("i64", "add"), ("u64", "min"), ("f64", "max"), ("f64", "add")]
 
 
 @pytest.mark.parametrize("dt,op", DEV_CASES)
 @pytest.mark.parametrize("inclusive", [False, True], ids=["excl", "incl"])
 def test_device_scan_tile_edges(dt, op, inclusive):
     e = 16 // np.dtype(oracle.STORAGE[dt]).itemsize
-    t = DEV_TILE_VECS * e
+    t = dev_tile_vecs(op) * e
     fn = sc.scan_device_inclusive if inclusive else sc.scan_device
     seed = 0
     for off in range(4 if e > 2 else e):
@@ -91,10 +96,10 @@ def test_device_scan_tile_edges(dt, op, inclusive):
             assert not big_out[:off].any() and not big_out[off + n:].any(), label + ": outside written"
 
 
-@pytest.mark.parametrize("dt,op", [("i32", "add"), ("i64", "max")])
+@pytest.mark.parametrize("dt,op", [("i32", "add"), ("i64", "max"), ("f64", "add")])
 def test_device_scan_tile_edges_one_element_vectors(dt, op):
-    # input and output phases differ: one element per vector, tiles of DEV_TILE_VECS elements
-    t = DEV_TILE_VECS
+    # input and output phases differ: one element per vector, tiles of as many elements
+    t = dev_tile_vecs(op)
     for i, n in enumerate(edge_sizes(t)):
         x = rand_input(dt, n, 71_000 + i)
         for inclusive in (False, True):
