@@ -58,15 +58,19 @@ def rand_input(dt, shape, seed):
 
 
 # covers every launch-shape boundary of the row kernel for 4- and 2-byte
-# elements (rows touching 64, 256, 1024 and 1280 16-byte vectors) and rows
-# long enough to take several chunks
+# elements (rows touching 64, 256, 320, 512, 768, 1024 and 1280 16-byte
+# vectors, with and without the line of slack that windows starting on a
+# 128-byte line add) and rows long enough to take several chunks
 ROW_SHAPES = [(1, 1), (1, 2), (3, 3), (3, 5), (1, 63), (3, 64), (5, 65), (2, 250), (3, 251),
               (3, 255), (3, 256), (3, 257), (2, 498), (3, 499), (2, 511), (3, 513), (2, 1018),
               (3, 1019), (2, 1023), (2, 1024), (3, 1025), (2, 2034), (3, 2035), (2, 2047),
               (3, 2049), (2, 4090), (3, 4091), (2, 4351), (2, 4352), (3, 4353), (2, 5114),
               (3, 5115), (2, 8178), (3, 8179), (2, 8703), (2, 8704), (3, 8705), (2, 10226),
               (3, 10227), (2, 20000), (3, 50001), (7, 333), (33, 100), (3, 4096), (3, 5120),
-              (3, 8192), (2, 10240), (2, 16384)]
+              (3, 8192), (2, 10240), (2, 16384), (3, 1249), (3, 1253), (2, 1277), (3, 1281),
+              (3, 2017), (2, 2045), (3, 2053), (3, 3041), (2, 3069), (3, 3077), (3, 2497),
+              (2, 2553), (3, 2569), (3, 4041), (2, 4093), (3, 4105), (3, 6089), (2, 6141),
+              (3, 6153)]
 
 
 DEV_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 4097, 8191, 8192, 8193,
