@@ -399,11 +399,11 @@ __global__ __launch_bounds__(64 * (WD + 1)) void scan_device_runs_kernel(
   }
 }
 
-// Tiles of tv vectors covering window elements [ph, n + ph) (ph < e) in
-// vectors of e elements.
-static int64_t tiles_for(int64_t n, int e, int64_t tv) {
+// Tiles of tv vectors covering window elements [ph, n + ph) in vectors of e
+// elements.
+static int64_t tiles_for(int64_t n, int64_t ph, int e, int64_t tv) {
   if (n <= 0) return 0;
-  const int64_t v_last = (n - 1 + (e - 1)) / e;
+  const int64_t v_last = (n + ph - 1) / e;
   return v_last / tv + 1;
 }
 
@@ -416,11 +416,13 @@ static int fmt_bytes(Fmt f) {
 }
 
 
-// Sized for the slowest path (one element per vector) and the smallest tile,
-// so one scratch size serves every pointer alignment and launch shape.
+// Sized for the slowest path (one element per vector, no phase) and the
+// smallest tile, so one scratch size serves every pointer alignment and launch
+// shape: with vectors of e >= 2 elements and a window phase below 128 bytes,
+// (n + ph - 1) / e never exceeds n - 1 by enough to need another tile.
 size_t scan_device_tiles(int64_t n, Fmt fmt) {
   (void)fmt;
-  return (size_t)tiles_for(n, 1, kDevMinTileVecs);
+  return (size_t)tiles_for(n, 0, 1, kDevMinTileVecs);
 }
 
 // Tile layout by operation, measured on MI355X (us per exclusive scan; runs
@@ -453,8 +455,15 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   uint64_t* desc = desc_base(scratch);
   const bool vec = (ia % 16) == (oa % 16);
   const int e = vec ? EV : 1;
-  const int64_t ph = vec ? (int64_t)((ia % 16) / sizeof(S)) : 0;
-  const int64_t ntiles = tiles_for(n, e, TV);
+  // The window starts on the 16-byte vector that holds the first element, or,
+  // when input and output share their place in a 128-byte line, on that
+  // line, so that every load and store instruction covers whole lines (one
+  // that starts mid-line touches nine lines per KiB instead of eight).  The
+  // window elements before the array are read (within the array's first line,
+  // so within its page) and masked as the identity; none is stored.
+  const bool line = (ia % 128) == (oa % 128);
+  const int64_t ph = vec ? (int64_t)((ia % (line ? 128 : 16)) / sizeof(S)) : 0;
+  const int64_t ntiles = tiles_for(n, ph, e, TV);
   hipError_t err = launch_fill_desc(desc, ntiles, Desc<typename F::W>::kWords, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));

@@ -12,7 +12,11 @@ for integers, min/max and select, within the float-add tolerance otherwise.
 
 Arrays that start inside a 16-byte vector are addressed through an aligned
 window that begins `ph` elements before the array, so their boundaries move to
-k*T - ph; each size list is repeated for in-phase offsets of 1-3 elements.
+k*T - ph; each size list is repeated for in-phase offsets of 1-3 elements.  The
+device scans start their window on the 128-byte line that holds the first
+element when input and output share their place in it, so for them ph is the
+element offset within the line, and offsets past the first vector are tested
+too.
 Arrays whose input and output phases differ run with one element per vector,
 so their tiles are as many elements as vectors.
 """
@@ -49,9 +53,9 @@ def _gpu():
 
 
 def views(n, dt, off_in, off_out):
-    """Zeroed device buffers of n + 8 elements and the n-element views at the offsets."""
-    big_in = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
-    big_out = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+    """Zeroed device buffers of n + 40 elements and the n-element views at the offsets."""
+    big_in = torch.zeros(n + 40, dtype=STORE_T[dt], device="cuda")
+    big_out = torch.zeros(n + 40, dtype=STORE_T[dt], device="cuda")
     return big_in, big_out, big_in[off_in:off_in + n], big_out[off_out:off_out + n]
 
 
@@ -82,8 +86,10 @@ def test_device_scan_tile_edges(dt, op, inclusive):
     t = dev_tile_vecs(op) * e
     fn = sc.scan_device_inclusive if inclusive else sc.scan_device
     seed = 0
-    for off in range(4 if e > 2 else e):
-        ph = off % e                    # the window phase of an array at element offset off
+    # offsets within the first vector, then past it (up to the end of a line)
+    offs = [0, 1, 2, 3, 5, 17, 31] if e == 4 else [0, 1, 3, 9, 15]
+    for off in offs:
+        ph = off                        # the window phase: the offset within the 128-byte line
         for n in edge_sizes(t, ph):
             seed += 1
             x = rand_input(dt, n, 70_000 + seed)
