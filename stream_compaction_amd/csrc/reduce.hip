@@ -120,8 +120,9 @@ __global__ __launch_bounds__(64) void reduce_final_kernel(uintptr_t partials, in
   if (lane == 0) *gptr<typename F::S>(out) = narrow<F>(acc);
 }
 
-// Launch geometry for n elements at pointer phase ph (elements past the last
-// 16-byte boundary before the array).  Never more workgroups than
+// Launch geometry for n elements at pointer phase ph (elements past the
+// 128-byte line boundary before the array: the window starts on the line, so
+// that every load instruction covers whole lines).  Never more workgroups than
 // min(ceil(runs / 4), kRedMaxBlocks), which grows with runs; the scratch size
 // takes that bound at the largest phase, which never needs fewer runs.
 struct RedGeom {
@@ -154,7 +155,8 @@ static int fmt_size(Fmt f) {
 
 size_t reduce_partials(int64_t n, Fmt fmt) {
   const int e = 16 / fmt_size(fmt);
-  const int64_t runs = red_geom(n, e, e - 1, (int64_t)kWave * kRedLoadsMin).runs;
+  const int64_t runs =
+      red_geom(n, e, 128 / fmt_size(fmt) - 1, (int64_t)kWave * kRedLoadsMin).runs;
   const int64_t bound = (runs + kRedWaves - 1) / kRedWaves;
   return (size_t)(bound < kRedMaxBlocks ? bound : kRedMaxBlocks);
 }
@@ -165,7 +167,10 @@ static hipError_t launch_red_t(const void* in, void* out, int64_t n, void* scrat
   using S = typename F::S;
   constexpr int EV = 16 / (int)sizeof(S);
   const uintptr_t ia = (uintptr_t)in;
-  const int64_t ph = (int64_t)((ia % 16) / sizeof(S));
+  // the window starts on the 128-byte line that holds the first element (the
+  // elements before the array are read within that line, so within its page,
+  // and masked as the identity)
+  const int64_t ph = (int64_t)((ia % 128) / sizeof(S));
   constexpr int L = red_loads<typename F::W, O>();
   static_assert(L >= kRedLoadsMin, "scratch is sized for the smallest run");
   const RedGeom g = red_geom(n, EV, ph, (int64_t)kWave * L);

@@ -373,14 +373,16 @@ __global__ __launch_bounds__(64 * (WD + 1), MINW) void reduce_by_key_kernel(
 
 __global__ void rbk_count_zero_kernel(int32_t* num_runs) { *num_runs = 0; }
 
-static int64_t rbk_tiles_for(int64_t n, int e, int64_t tv) {
+// Tiles of tv vectors covering window elements [ph, n + ph) in vectors of e.
+static int64_t rbk_tiles_for(int64_t n, int64_t ph, int e, int64_t tv) {
   if (n <= 0) return 0;
-  const int64_t v_last = (n - 1 + (e - 1)) / e;
+  const int64_t v_last = (n + ph - 1) / e;
   return v_last / tv + 1;
 }
 
-// Sized for the one-element-per-vector path and the smallest tile.
-size_t reduce_by_key_tiles(int64_t n) { return (size_t)rbk_tiles_for(n, 1, kRbkMinTileVecs); }
+// Sized for the one-element-per-vector path (no phase) and the smallest tile;
+// four-element vectors at a phase below 32 elements never need more tiles.
+size_t reduce_by_key_tiles(int64_t n) { return (size_t)rbk_tiles_for(n, 0, 1, kRbkMinTileVecs); }
 
 template <class KF, class VF, int WD, int K, int FL, int MINW>
 static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* keys_out,
@@ -390,8 +392,12 @@ static hipError_t launch_rbk_cfg(const void* keys, const void* values, void* key
   const uintptr_t ka = (uintptr_t)keys, va = (uintptr_t)values;
   const bool vec = (ka % 16) == (va % 16);
   const int e = vec ? 4 : 1;
-  const int64_t ph = vec ? (int64_t)((ka % 16) / 4) : 0;
-  const int64_t ntiles = rbk_tiles_for(n, e, TV);
+  // the window starts on the 128-byte line of the first key when the values
+  // share its place in a line (the elements before the arrays are read within
+  // their first lines, so within their pages, and take no part in any run)
+  const bool line = (ka % 128) == (va % 128);
+  const int64_t ph = vec ? (int64_t)((ka % (line ? 128 : 16)) / 4) : 0;
+  const int64_t ntiles = rbk_tiles_for(n, ph, e, TV);
   uint64_t* desc = desc_base(scratch);
   hipError_t err = launch_fill_desc(desc, ntiles, Desc<Seg<float>>::kWords, stream);
   if (err != hipSuccess) return err;

@@ -401,19 +401,20 @@ __global__ __launch_bounds__(64 * (WD + 1)) void select_kernel(uintptr_t in_base
   }
 }
 
-// Tiles of tv vectors covering window elements [ph, n + ph) (ph < e).
-static int64_t sel_tiles_for(int64_t n, int e, int64_t tv) {
+// Tiles of tv vectors covering window elements [ph, n + ph) in vectors of e.
+static int64_t sel_tiles_for(int64_t n, int64_t ph, int e, int64_t tv) {
   if (n <= 0) return 0;
-  const int64_t v_last = (n - 1 + (e - 1)) / e;
+  const int64_t v_last = (n + ph - 1) / e;
   return v_last / tv + 1;
 }
 
-// Sized for 16-byte elements (one per vector, the most tiles) and the
-// smallest tile, so one scratch size serves every element width and launch
+// Sized for 16-byte elements (one per vector, the most tiles) at the largest
+// window phase they can take (seven vectors into a line) and the smallest
+// tile, so one scratch size serves every element width, alignment and launch
 // shape.
 size_t select_tiles(int64_t n, size_t elem_bytes) {
   (void)elem_bytes;
-  return (size_t)sel_tiles_for(n, 1, kSelMinTileVecs);
+  return (size_t)sel_tiles_for(n, 7, 1, kSelMinTileVecs);
 }
 
 __global__ void store_count_zero_kernel(int32_t* num_out) { *num_out = 0; }
@@ -427,11 +428,17 @@ static hipError_t launch_sel_cfg(const void* in, const uint8_t* flags, void* out
   constexpr int E = sel_e<EB>(), VB = E * EB;
   constexpr int64_t TV = (int64_t)kWave * kSelJ * C * WD;
   const uintptr_t ia = (uintptr_t)in, fa = (uintptr_t)flags, oa = (uintptr_t)out;
-  const int64_t ph = (int64_t)((ia % VB) / EB);
+  // The payload window starts on the payload vector that holds the first
+  // element or, when the flags before the array's first flag stay inside the
+  // flags' own 128-byte line (so inside their page), on the payload's 128-byte
+  // line, so that every payload load covers whole lines.  The elements before
+  // the array are never selected.
+  const int64_t lph = (int64_t)((ia % 128) / EB);
+  const int64_t ph = (int64_t)(fa % 128) >= lph ? lph : (int64_t)((ia % VB) / EB);
   const int64_t out_ph = (int64_t)((oa % VB) / EB);
   const uintptr_t fbase = fa - (uintptr_t)ph;          // flag byte of window element 0
   const bool fvec = (fbase % E) == 0;
-  const int64_t ntiles = sel_tiles_for(n, E, TV);
+  const int64_t ntiles = sel_tiles_for(n, ph, E, TV);
   uint64_t* desc = desc_base(scratch);
   hipError_t err = launch_fill_desc(desc, ntiles, Desc<uint32_t>::kWords, stream);
   if (err != hipSuccess) return err;

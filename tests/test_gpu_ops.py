@@ -143,11 +143,11 @@ def test_device_inclusive_minmax_full(which, op):
 
 def test_device_inclusive_misaligned_views():
     for dt in ("i32", "i64", "f32"):
-        for off_in, off_out in ((1, 1), (1, 0), (0, 3)):
+        for off_in, off_out in ((1, 1), (1, 0), (0, 3), (9, 9)):
             n = 100_003
             x = rand_input(dt, n, 98)
-            big_in = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
-            big_out = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+            big_in = torch.zeros(n + 16, dtype=STORE_T[dt], device="cuda")
+            big_out = torch.zeros(n + 16, dtype=STORE_T[dt], device="cuda")
             xin = big_in[off_in:off_in + n]
             xin.copy_(to_dev(x, dt))
             yout = big_out[off_out:off_out + n]
@@ -245,10 +245,10 @@ def test_reduce_workload4_full(which, op):
 
 def test_reduce_misaligned_views():
     for dt in ("i32", "i64", "f32", "f64"):
-        for off in (1, 2, 3):
+        for off in (1, 2, 3, 7, 15):
             n = 1_000_003
             x = rand_input(dt, n, 97)
-            big = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+            big = torch.zeros(n + 16, dtype=STORE_T[dt], device="cuda")
             xin = big[off:off + n]
             xin.copy_(to_dev(x, dt))
             for op in ("add", "min", "max"):
@@ -386,9 +386,9 @@ def test_reduce_by_key_misaligned_and_aliased():
     n = 200_003
     keys = run_lengths_keys(n, 5, 77)
     values = rbk_values(n, "i32", 78)
-    for off_k, off_v in ((1, 1), (0, 3), (2, 1)):
-        bk = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
-        bv = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
+    for off_k, off_v in ((1, 1), (0, 3), (2, 1), (21, 21), (21, 5)):
+        bk = torch.zeros(n + 32, dtype=torch.int32, device="cuda")
+        bv = torch.zeros(n + 32, dtype=torch.int32, device="cuda")
         kin, vin = bk[off_k:off_k + n], bv[off_v:off_v + n]
         kin.copy_(torch.from_numpy(keys).cuda())
         vin.copy_(torch.from_numpy(values).cuda())

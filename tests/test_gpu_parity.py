@@ -200,11 +200,11 @@ def test_device_workload4_full(which, op):
 
 def test_device_misaligned_views():
     for dt in ("i32", "i64", "f32"):
-        for off_in, off_out in ((1, 1), (1, 0), (0, 3), (2, 2)):
+        for off_in, off_out in ((1, 1), (1, 0), (0, 3), (2, 2), (13, 13), (13, 5), (31, 31)):
             n = 100_003
             x = rand_input(dt, n, 99)
-            big_in = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
-            big_out = torch.zeros(n + 8, dtype=STORE_T[dt], device="cuda")
+            big_in = torch.zeros(n + 40, dtype=STORE_T[dt], device="cuda")
+            big_out = torch.zeros(n + 40, dtype=STORE_T[dt], device="cuda")
             xin = big_in[off_in:off_in + n]
             xin.copy_(to_dev(x, dt))
             yout = big_out[off_out:off_out + n]
@@ -313,10 +313,11 @@ def test_select_misaligned_views_all_widths(eb):
     ora, ko = oracle.select(xb.reshape(-1).view(np.dtype((np.void, eb))), flags)
     want = np.ascontiguousarray(ora).view(np.uint8).reshape(n, eb)
     dt = SEL_NP[eb]
-    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1)):
-        big_in = torch.zeros(n + 8, dtype=torch.from_numpy(np.zeros(1, dt)).dtype, device="cuda")
-        big_f = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
-        fill = np.full((n + 8) * eb, 7, np.uint8).view(dt)
+    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1),
+                                    (17, 17, 17), (17, 3, 5), (31, 30, 31), (9, 40, 2)):
+        big_in = torch.zeros(n + 48, dtype=torch.from_numpy(np.zeros(1, dt)).dtype, device="cuda")
+        big_f = torch.zeros(n + 48, dtype=torch.uint8, device="cuda")
+        fill = np.full((n + 48) * eb, 7, np.uint8).view(dt)
         big_out = torch.from_numpy(fill).cuda()
         big_in[off_in:off_in + n].copy_(torch.from_numpy(xb.reshape(-1).view(dt).copy()).cuda())
         big_f[off_f:off_f + n].copy_(torch.from_numpy(flags).cuda())
@@ -324,7 +325,7 @@ def test_select_misaligned_views_all_widths(eb):
                                    out=big_out[off_out:off_out + n])
         k = int(num.item())
         assert k == ko
-        got = big_out.cpu().numpy().view(np.uint8).reshape(n + 8, eb)
+        got = big_out.cpu().numpy().view(np.uint8).reshape(n + 48, eb)
         label = f"select eb={eb} offsets {off_in},{off_f},{off_out}"
         check_exact(got[off_out:off_out + k].reshape(-1), want[:k].reshape(-1), label)
         assert (got[:off_out] == 7).all() and (got[off_out + k:] == 7).all(), label
@@ -355,10 +356,11 @@ def test_select_misaligned_views():
     x = rng.integers(0, 1 << 31, size=n, dtype=np.int64).astype(np.int32)
     flags = workloads.bernoulli_flags(n, 0.5, 10)
     ora, ko = oracle.select(x, flags)
-    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1)):
-        big_in = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
-        big_f = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
-        big_out = torch.full((n + 8,), 7, dtype=torch.int32, device="cuda")
+    for off_in, off_f, off_out in ((1, 1, 1), (1, 0, 3), (0, 3, 2), (3, 2, 0), (2, 5, 1),
+                                    (17, 17, 17), (17, 3, 5), (31, 30, 31), (9, 40, 2)):
+        big_in = torch.zeros(n + 48, dtype=torch.int32, device="cuda")
+        big_f = torch.zeros(n + 48, dtype=torch.uint8, device="cuda")
+        big_out = torch.full((n + 48,), 7, dtype=torch.int32, device="cuda")
         xin = big_in[off_in:off_in + n]
         xin.copy_(torch.from_numpy(x).cuda())
         fin = big_f[off_f:off_f + n]

@@ -135,16 +135,16 @@ def run_select_view(xb, flags, eb, off, label):
     """xb: uint8 [n, eb]; payload, flags and output all at element offset `off`."""
     n = xb.shape[0]
     tdt = torch.from_numpy(np.zeros(1, SEL_NP[eb])).dtype
-    big_in = torch.zeros(n + 8, dtype=tdt, device="cuda")
-    big_f = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
-    big_out = torch.from_numpy(np.full((n + 8) * eb, SENTINEL, np.uint8).view(SEL_NP[eb])).cuda()
+    big_in = torch.zeros(n + 128, dtype=tdt, device="cuda")
+    big_f = torch.zeros(n + 136, dtype=torch.uint8, device="cuda")
+    big_out = torch.from_numpy(np.full((n + 128) * eb, SENTINEL, np.uint8).view(SEL_NP[eb])).cuda()
     big_in[off:off + n].copy_(torch.from_numpy(xb.reshape(-1).view(SEL_NP[eb]).copy()).cuda())
     big_f[off:off + n].copy_(torch.from_numpy(flags).cuda())
     _, num = sc.select_compact(big_in[off:off + n], big_f[off:off + n], out=big_out[off:off + n])
     k = int(num.item())
     ora, ko = oracle.select(xb.reshape(-1).view(np.dtype((np.void, eb))), flags)
     assert k == ko, f"{label}: count {k} != {ko}"
-    got = big_out.cpu().numpy().view(np.uint8).reshape(n + 8, eb)
+    got = big_out.cpu().numpy().view(np.uint8).reshape(n + 128, eb)
     want = np.ascontiguousarray(ora).view(np.uint8).reshape(n, eb)
     check_exact(got[off:off + k].reshape(-1), want[:k].reshape(-1), label)
     assert (got[:off] == SENTINEL).all() and (got[off + k:] == SENTINEL).all(), \
@@ -157,8 +157,11 @@ def test_select_tile_edges(eb, p):
     e = sel_elems(eb)
     t = SEL_TILE_VECS * e
     seed = 0
-    for off in range(4 if e > 1 else 1):
-        ph = off % e
+    # offsets within the first payload vector, then past it: the window then
+    # starts on the payload's 128-byte line, ph elements before the array
+    line = 128 // eb
+    for off in sorted({0, 1, 2, 3, line // 4 + 1, line - 1} if e > 1 else {0, 3, line - 1}):
+        ph = off % line
         for n in edge_sizes(t, ph):
             seed += 1
             rng = np.random.default_rng(72_000 + seed)
@@ -181,8 +184,8 @@ def rbk_case(n, mean_run, seed):
 
 def run_rbk_view(keys, values, off_k, off_v, vd, label):
     n = keys.size
-    bk = torch.zeros(n + 8, dtype=torch.int32, device="cuda")
-    bv = torch.zeros(n + 8, dtype=STORE_T[vd], device="cuda")
+    bk = torch.zeros(n + 40, dtype=torch.int32, device="cuda")
+    bv = torch.zeros(n + 40, dtype=STORE_T[vd], device="cuda")
     bk[off_k:off_k + n].copy_(torch.from_numpy(keys).cuda())
     bv[off_v:off_v + n].copy_(to_dev(values, vd))
     ko = torch.full((n,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
@@ -207,7 +210,9 @@ def run_rbk_view(keys, values, off_k, off_v, vd, label):
 def test_reduce_by_key_tile_edges(mean_run):
     t = RBK_TILE_VECS * 4
     seed = 0
-    for ph in range(4):
+    # offsets within the first vector, then past it (the window starts on the
+    # keys' 128-byte line when the values share it)
+    for ph in (0, 1, 2, 3, 9, 31):
         for n in edge_sizes(t, ph):
             seed += 1
             keys, values = rbk_case(n, mean_run, 74_000 + seed + 100 * mean_run)
