@@ -125,6 +125,27 @@ def test_rows_misaligned_views():
             assert not big_out[:off_out].any() and not big_out[off_out + rows * n:].any()
 
 
+@pytest.mark.parametrize("n", [3000, 8191, 16383])
+def test_rows_misaligned_long_rows(n):
+    # long rows whose windows start on the 128-byte line before each row:
+    # equal phases (16-byte vectors) and unequal ones (one element per vector)
+    for dt in ("f32", "bf16"):
+        rows = 7
+        x = rand_input(dt, (rows * n,), 78 + n)
+        for off_in, off_out in ((0, 0), (1, 1), (5, 5), (13, 13), (1, 2), (0, 3)):
+            big_in = torch.zeros(rows * n + 16, dtype=STORE_T[dt], device="cuda")
+            big_out = torch.zeros(rows * n + 16, dtype=STORE_T[dt], device="cuda")
+            xin = big_in[off_in:off_in + rows * n]
+            xin.copy_(to_dev(x, dt))
+            yout = big_out[off_out:off_out + rows * n]
+            for op, excl in (("add", True), ("max", False)):
+                sc.scan_rows(xin.view(rows, n), op=op, exclusive=excl, out=yout.view(rows, n))
+                torch.cuda.synchronize()
+                compare_scan(from_dev(yout, dt).reshape(rows, n), x.reshape(rows, n), dt, op, excl,
+                             f"long rows {dt} [{rows},{n}] {op} in+{off_in} out+{off_out}")
+            assert not big_out[:off_out].any() and not big_out[off_out + rows * n:].any()
+
+
 def test_rows_signed_zero_and_inf():
     vals = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0], np.float32)
     rng = np.random.default_rng(5)

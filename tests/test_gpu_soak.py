@@ -8,8 +8,10 @@ stale descriptor, a store that lands late) shows up only now and then.  Each
 test below draws at least 100 counts log-uniformly from [1, 2^26] (plus a few
 full-size calls), runs them back to back with one scratch buffer that is never
 cleared by the caller, and checks every output against the oracle.  Inputs are
-slices of one seeded pool at random element offsets, so every window phase
-and both the vector and the one-element-per-vector paths come up.  The
+slices of one seeded pool at random element offsets (up to 40, past a
+128-byte line for 4-byte elements), and outputs alternate between the same
+offset and offset 0, so every window phase, windows on lines, and both the
+vector and the one-element-per-vector paths come up.  The
 64-bit-descriptor path (i64 values, reduce-by-key's pairs) is covered too.
 """
 import numpy as np
@@ -38,15 +40,15 @@ def _gpu():
 
 
 def draws(seed, iters=ITERS, nmax=NMAX):
-    """(n, offset) pairs: n log-uniform in [1, nmax], offset in [0, 8)."""
+    """(n, offset) pairs: n log-uniform in [1, nmax], offset in [0, 40)."""
     rng = np.random.default_rng(seed)
     ns = np.exp(rng.uniform(0, np.log(nmax), size=iters)).astype(np.int64)
-    return [(int(max(1, n)), int(o)) for n, o in zip(ns, rng.integers(0, 8, size=iters))]
+    return [(int(max(1, n)), int(o)) for n, o in zip(ns, rng.integers(0, 40, size=iters))]
 
 
 @pytest.mark.parametrize("dt,op", [("i32", "add"), ("i64", "min")])
 def test_soak_scan_device(dt, op):
-    pool_n = NMAX + 8
+    pool_n = NMAX + 40
     pool = workloads.uniform_ints(pool_n, 0, 15, 90_001) if dt == "i32" else \
         np.random.default_rng(90_002).integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max,
                                                size=pool_n, dtype=np.int64, endpoint=True)
@@ -57,8 +59,10 @@ def test_soak_scan_device(dt, op):
     for it, (n, off) in enumerate(draws(91_000 + len(dt))):
         if it % 20 == 0:
             note(f"soak scan_device {dt} {op}: call {it}, n={n}, offset {off}")
-        sc.scan_device(pd[off:off + n], op=op, out=out[:n], scratch=scratch, dtype=dt)
-        got = out[:n].cpu().numpy()
+        # even calls: output at the input's offset (windows on lines), odd: at 0
+        o = out[off:off + n] if it % 2 == 0 else out[:n]
+        sc.scan_device(pd[off:off + n], op=op, out=o, scratch=scratch, dtype=dt)
+        got = o.cpu().numpy()
         check_exact(got, oracle.scan(pool[off:off + n], dt, op, exclusive=True),
                     f"soak scan_device {dt} {op} call {it} n={n} offset {off}")
     del pd, out
@@ -79,7 +83,7 @@ def test_soak_scan_device(dt, op):
 
 
 def test_soak_select():
-    pool_n = NMAX + 8
+    pool_n = NMAX + 40
     payload = np.random.default_rng(92_001).integers(0, 1 << 32, size=pool_n,
                                                      dtype=np.uint64).astype(np.uint32)
     level = np.random.default_rng(92_002).integers(0, 256, size=pool_n, dtype=np.uint8)
@@ -94,13 +98,21 @@ def test_soak_select():
         thr = int(thresholds[it])
         if it % 20 == 0:
             note(f"soak select: call {it}, n={n}, offset {off}, threshold {thr}")
-        fd = (ld[off:off + n] < thr).to(torch.uint8)
-        sc.select_compact(pd[off:off + n], fd, out=out[:n], num_out=num, scratch=scratch)
+        # even calls: flags a slice of a pool-sized array at the payload's offset
+        # (so the payload window can start on its line) and output at that
+        # offset too; odd calls: fresh flags and output at 0
+        if it % 2 == 0:
+            fd = (ld < thr).to(torch.uint8)[off:off + n]
+            o = out[off:off + n]
+        else:
+            fd = (ld[off:off + n] < thr).to(torch.uint8)
+            o = out[:n]
+        sc.select_compact(pd[off:off + n], fd, out=o, num_out=num, scratch=scratch)
         k = int(num.item())
         fl = (level[off:off + n] < thr).astype(np.uint8)
         want, kw = oracle.select(payload[off:off + n], fl)
         assert k == kw, f"soak select call {it} n={n}: count {k} != {kw}"
-        check_exact(out[:k].cpu().numpy().view(np.uint32), want[:k],
+        check_exact(o[:k].cpu().numpy().view(np.uint32), want[:k],
                     f"soak select call {it} n={n} offset {off}")
     del pd, ld, out
     p, f = workloads.sel_inputs(workloads.FULL["sel"], 0.5)
@@ -117,7 +129,7 @@ def test_soak_select():
 
 
 def test_soak_reduce_by_key():
-    pool_n = NMAX + 8
+    pool_n = NMAX + 40
     rng = np.random.default_rng(94_001)
     lengths = rng.geometric(1.0 / 8, size=pool_n // 4)
     keys = np.repeat(rng.integers(0, 1 << 20, size=lengths.size), lengths)[:pool_n].astype(np.int32)
