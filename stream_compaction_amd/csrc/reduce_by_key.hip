@@ -128,17 +128,6 @@ __global__ __launch_bounds__(64 * (WD + 1), MINW) void reduce_by_key_kernel(
   }
   __syncthreads();
 
-  // K key and value vectors of the run of 64*K vectors starting at `first`.
-  auto load = [&](int64_t first, Raw (&rk)[K], Raw (&rv)[K]) {
-    const int64_t left = v_last + 1 - first;
-    const int64_t nv = left <= 0 ? 0 : (left < kWaveVecs ? left : kWaveVecs);
-    const Buf bk(k_base + first * VB, nv * VB), bv(v_base + first * VB, nv * VB);
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      rk[j] = IO::load(bk, (uint32_t)((j * kWave + lane) * VB));
-      rv[j] = IO::load(bv, (uint32_t)((j * kWave + lane) * VB));
-    }
-  };
   // Run-start bits (bit k: element k of the lane's vector) of load j, whose
   // first vector is jv; `prev` is the key before the load's first element.
   auto heads = [&](int64_t jv, const Raw& rk, uint32_t prev) -> uint32_t {

@@ -407,15 +407,6 @@ static int64_t tiles_for(int64_t n, int64_t ph, int e, int64_t tv) {
   return v_last / tv + 1;
 }
 
-static int fmt_bytes(Fmt f) {
-  switch (f) {
-    case Fmt::F16: case Fmt::BF16: return 2;
-    case Fmt::F64: case Fmt::I64: case Fmt::U64: return 8;
-    default: return 4;
-  }
-}
-
-
 // Sized for the slowest path (one element per vector, no phase) and the
 // smallest tile, so one scratch size serves every pointer alignment and launch
 // shape: with vectors of e >= 2 elements and a window phase below 128 bytes,
