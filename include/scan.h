@@ -20,6 +20,11 @@
  *    exclusive scan's output must be a distinct buffer from its input
  *    ("Algorithms" page, section qd.algorithms.exclusive_scan_{add,min,max},
  *    its list of constraints).
+ *  - Input arrays are read in whole 16-byte vectors, which may include bytes
+ *    just outside an array's range but never outside the 128-byte lines that
+ *    hold its first and last bytes (so never outside their pages); those
+ *    bytes are ignored.  Nothing outside an output array's range is ever
+ *    written.
  *  - Sizes: 0 <= n <= INT32_MAX (the pages index and count with 32-bit
  *    integers: "Algorithms" page, section "Capacity (log256_max_n)", and the
  *    i32 count of select).  n == 0 (or rows == 0) is a valid no-op ("Tile
