@@ -23,9 +23,11 @@ size_t scan_device_tiles(int64_t n, Fmt fmt);       // descriptors needed
 // n_dev (all launchers below): when not null, the live count is read from it
 // on the device and clamped to [0, n]; n is then the capacity that grids and
 // scratch are sized for.
+// descs_clear: the caller has already zeroed the first scan_device_tiles(n,
+// fmt) descriptors of `scratch` earlier on `stream`, so no fill kernel runs.
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
                               bool inclusive, void* scratch, hipStream_t stream,
-                              const int32_t* n_dev = nullptr);
+                              const int32_t* n_dev = nullptr, bool descs_clear = false);
 
 // Device-wide reduction into out[0]; op: 0 add, 1 min, 2 max.  n == 0 writes
 // the identity.  Scratch holds one partial per workgroup of the first launch.

@@ -68,14 +68,20 @@ __device__ __forceinline__ int64_t rx_xcd_tile(int64_t b, int64_t ntiles) {
 // ---------------------------------------------------------------------------
 // 1. tile histograms, digit-major
 // ---------------------------------------------------------------------------
+// It also zeroes the descriptors of the device scan that follows it on the
+// stream (workgroup b clears descriptors b, b + grid, ...), so that scan needs
+// no fill kernel of its own.
 template <class KT, KeyKind KK, int WAVES, int KPT>
 __global__ __launch_bounds__(64 * WAVES) void radix_tile_hist_kernel(
     const KT* __restrict__ kin, int64_t n_cap, const int32_t* n_dev, int shift, int64_t ntiles,
-    uint32_t* hist) {
+    uint32_t* hist, uint64_t* scan_desc, int64_t scan_ndesc) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kTile = kThreads * KPT;
   __shared__ uint32_t s_h[WAVES][kRxBins];
   const int tid = threadIdx.x, wave = wave_id();
+  if (tid == 0) {
+    for (int64_t d = blockIdx.x; d < scan_ndesc; d += gridDim.x) scan_desc[d * kDescLineWords] = 0ull;
+  }
   const int64_t tile = rx_xcd_tile(blockIdx.x, ntiles);
   const int64_t t0 = tile * kTile;
   const int64_t n = live_count(n_cap, n_dev);
@@ -534,6 +540,10 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
   uint32_t* hist = (uint32_t*)scratch;
   uint32_t* offs = (uint32_t*)((char*)scratch + rx_hist_bytes(ntiles));
   void* scan_scratch = (char*)scratch + 2 * rx_hist_bytes(ntiles);
+  // the histogram kernel clears the scan's descriptors (one word each)
+  static_assert(Desc<uint32_t>::kWords == 1, "one descriptor word per tile");
+  uint64_t* const scan_desc = desc_base(scan_scratch);
+  const int64_t scan_ndesc = (int64_t)scan_device_tiles(ntiles * kRxBins, Fmt::U32);
   KT* src = (KT*)keys;
   KT* dst = (KT*)tmp_keys;
   void* vsrc = values;
@@ -544,11 +554,11 @@ static hipError_t launch_rx_t(void* keys, void* tmp_keys, void* values, void* tm
   for (int p = 0; p < npass; ++p) {
     constexpr int HW = RxHistShape<KT, VB>::kWaves, HKPT = RxHistShape<KT, VB>::kKpt;
     radix_tile_hist_kernel<KT, KK, HW, HKPT><<<dim3((unsigned)ntiles), dim3(64 * HW), 0, stream>>>(
-        src, n, n_dev, 8 * p, ntiles, hist);
+        src, n, n_dev, 8 * p, ntiles, hist, scan_desc, scan_ndesc);
     err = hipGetLastError();
     if (err == hipSuccess)
       err = launch_scan_device(hist, offs, ntiles * kRxBins, Fmt::U32, 0, false, scan_scratch,
-                               stream);
+                               stream, nullptr, true);
     if (err != hipSuccess) return err;
     if (b32) {
       radix_scatter_kernel<KT, KK, VB, W, KPT, true><<<dim3((unsigned)ntiles), dim3(64 * W), 0, stream>>>(

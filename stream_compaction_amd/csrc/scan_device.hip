@@ -435,7 +435,7 @@ constexpr bool kSideBySide = O == Op::Add;
 
 template <class F, Op O, bool INCL>
 static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scratch,
-                                 hipStream_t stream, const int32_t* n_dev) {
+                                 hipStream_t stream, const int32_t* n_dev, bool descs_clear) {
   using S = typename F::S;
   constexpr bool kSide = kSideBySide<O>;
   constexpr int WD = kSide ? 8 : 11;    // data waves (plus the look-back wave)
@@ -455,8 +455,10 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
   const bool line = (ia % 128) == (oa % 128);
   const int64_t ph = vec ? (int64_t)((ia % (line ? 128 : 16)) / sizeof(S)) : 0;
   const int64_t ntiles = tiles_for(n, ph, e, TV);
-  hipError_t err = launch_fill_desc(desc, ntiles, Desc<typename F::W>::kWords, stream);
-  if (err != hipSuccess) return err;
+  if (!descs_clear) {
+    const hipError_t err = launch_fill_desc(desc, ntiles, Desc<typename F::W>::kWords, stream);
+    if (err != hipSuccess) return err;
+  }
   const dim3 grid((unsigned)ntiles), block(64 * (WD + 1));
   const uintptr_t ib = vec ? ia - ph * sizeof(S) : ia, ob = vec ? oa - ph * sizeof(S) : oa;
   if constexpr (kSide) {
@@ -477,31 +479,32 @@ static hipError_t launch_dev_cfg(const void* in, void* out, int64_t n, void* scr
 
 template <class F, Op O>
 static hipError_t launch_dev_t(const void* in, void* out, int64_t n, bool incl, void* scratch,
-                               hipStream_t stream, const int32_t* n_dev) {
-  return incl ? launch_dev_cfg<F, O, true>(in, out, n, scratch, stream, n_dev)
-              : launch_dev_cfg<F, O, false>(in, out, n, scratch, stream, n_dev);
+                               hipStream_t stream, const int32_t* n_dev, bool descs_clear) {
+  return incl ? launch_dev_cfg<F, O, true>(in, out, n, scratch, stream, n_dev, descs_clear)
+              : launch_dev_cfg<F, O, false>(in, out, n, scratch, stream, n_dev, descs_clear);
 }
 
 template <class F>
 static hipError_t launch_dev_f(const void* in, void* out, int64_t n, int op, bool incl,
-                               void* scratch, hipStream_t stream, const int32_t* n_dev) {
+                               void* scratch, hipStream_t stream, const int32_t* n_dev,
+                               bool descs_clear) {
   switch (op) {
-    case 0: return launch_dev_t<F, Op::Add>(in, out, n, incl, scratch, stream, n_dev);
-    case 1: return launch_dev_t<F, Op::Min>(in, out, n, incl, scratch, stream, n_dev);
-    default: return launch_dev_t<F, Op::Max>(in, out, n, incl, scratch, stream, n_dev);
+    case 0: return launch_dev_t<F, Op::Add>(in, out, n, incl, scratch, stream, n_dev, descs_clear);
+    case 1: return launch_dev_t<F, Op::Min>(in, out, n, incl, scratch, stream, n_dev, descs_clear);
+    default: return launch_dev_t<F, Op::Max>(in, out, n, incl, scratch, stream, n_dev, descs_clear);
   }
 }
 
 hipError_t launch_scan_device(const void* in, void* out, int64_t n, Fmt fmt, int op,
                               bool inclusive, void* scratch, hipStream_t stream,
-                              const int32_t* n_dev) {
+                              const int32_t* n_dev, bool descs_clear) {
   switch (fmt) {
-    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, inclusive, scratch, stream, n_dev);
-    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, inclusive, scratch, stream, n_dev);
-    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, inclusive, scratch, stream, n_dev);
-    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, inclusive, scratch, stream, n_dev);
-    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, inclusive, scratch, stream, n_dev);
-    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream, n_dev);
+    case Fmt::I32: return launch_dev_f<FmtI32>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
+    case Fmt::U32: return launch_dev_f<FmtU32>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
+    case Fmt::F32: return launch_dev_f<FmtF32>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
+    case Fmt::I64: return launch_dev_f<FmtI64>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
+    case Fmt::U64: return launch_dev_f<FmtU64>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
+    case Fmt::F64: return launch_dev_f<FmtF64>(in, out, n, op, inclusive, scratch, stream, n_dev, descs_clear);
     default: return hipErrorInvalidValue;
   }
 }
