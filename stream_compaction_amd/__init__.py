@@ -23,7 +23,11 @@ Entry points (same names as the C ABI):
   scratch=None)`` - stable ascending sort of a 1-D tensor of 32/64-bit keys in
   place, carrying values along.
 * ``select_compact(x, flags, out=None, num_out=None, scratch=None)`` - stable
-  stream compaction of a 1-D tensor with 4- or 8-byte elements by uint8 flags.
+  stream compaction of a 1-D tensor with elements of 1, 2, 4, 8 or 16 bytes by
+  uint8 flags (elements move as raw bits).
+* ``scan_device_noalloc(x, op="add", out=None)`` - ``scan_device`` on the
+  library's own per-GPU scratch, for callers that cannot allocate (calls that
+  overlap on one GPU race).
 * ``*_devn`` variants of the device-wide calls (C ABI names; ``n_live`` a
   1-element int32 GPU tensor, ``capacity`` the tensors' length): the count is
   read on the device, so one captured graph serves every count up to the
