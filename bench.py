@@ -131,6 +131,12 @@ def pmc_summary(fetch_csv, write_csv, command, select_key="select_p0.5"):
     print(json.dumps(out))
 
 
+class CallTimes(list):
+    """Per-call times (ms) of the eager pass, plus the graph region's average
+    per call in `window_ms`."""
+    window_ms = None
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -229,14 +235,15 @@ def main():
     def timed(launch, steps, warmup):
         """Time `steps` calls of launch(i) after `warmup` untimed ones.
 
-        Returns (wall seconds, per-call kernel ms list).  The timed region is
-        bracketed by synchronizations and holds the `steps` calls back to back:
-        captured once into a HIP graph and replayed (so host-side launch cost
-        does not stretch short kernels), or issued one by one with --eager.
-        One pair of HIP events on the launch stream brackets the region; a
-        second, eager pass brackets each call with its own pair of events.
-        The per-call figure is the smaller of the region average and the mean
-        of the per-call pairs (both include some dispatch overhead).
+        Returns (wall seconds, CallTimes).  The timed region is bracketed by
+        synchronizations and holds the `steps` calls back to back: captured
+        once into a HIP graph and replayed (so host-side launch cost does not
+        stretch short kernels), or issued one by one with --eager.  One pair
+        of HIP events on the launch stream brackets the region (its average
+        per call is `window_ms`); a second, eager pass brackets each call with
+        its own pair of events (the list itself).  The per-call figure the
+        results use is the smaller of the region average and the mean of the
+        per-call pairs (both include some dispatch overhead).
         """
         for i in range(warmup):
             launch(i)
@@ -270,9 +277,8 @@ def main():
             launch(i)
             ev1[i].record(cur)
         torch.cuda.synchronize()
-        per = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
-        if window_ms < float(np.mean(per)):
-            per = [window_ms] * steps
+        per = CallTimes(a.elapsed_time(b) for a, b in zip(ev0, ev1))
+        per.window_ms = window_ms
         return wall, per
 
     def bf16_dev(bits):
@@ -282,8 +288,14 @@ def main():
 
     def record(name, elems, algo_bytes, wall, per_ms, steps, note=""):
         avg_ms = float(np.mean(per_ms))
+        window_ms = getattr(per_ms, "window_ms", None)
+        if window_ms is not None and window_ms < avg_ms:
+            avg_ms = window_ms
         r = {"elements": int(elems), "algorithmic_bytes": int(algo_bytes),
-             "kernel_ms_avg": round(avg_ms, 5), "kernel_ms_min": round(float(np.min(per_ms)), 5),
+             "kernel_ms_avg": round(avg_ms, 5),
+             # each call between its own pair of events (dispatch included)
+             "call_ms_median": round(float(np.median(per_ms)), 5),
+             "call_ms_min": round(float(np.min(per_ms)), 5),
              "elements_per_s": elems / (avg_ms * 1e-3),
              "GBps": algo_bytes / (avg_ms * 1e-3) / 1e9,
              "frac_of_peak": algo_bytes / (avg_ms * 1e-3) / 1e9 / PEAK_GBS,
